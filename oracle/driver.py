@@ -1,0 +1,91 @@
+"""Run one CSA2 step of a workload through the oracle.
+
+TEST INFRASTRUCTURE ONLY (see the oracle package header).
+
+``inp`` is any object with the seeded-input interface (``wl`` plus
+``latent(b, start, stop)``, ``pair_logits()``, ``w_ik()``, ``q(l)``,
+``q_idx(l)``, ``head_w(l)``, ``swa(l)``); the driver reads arrays from it and
+imports nothing from the product.
+
+A step is: compress the new latent rows into the cache (the cache already
+holds every earlier entry), then run the layer group for the queries at the
+last ``n_q`` positions.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import csa2
+
+
+def dims_of(wl) -> csa2.Dims:
+    return csa2.Dims(
+        d=wl.d, d_rope=wl.d_rope, n_heads=wl.n_heads, n_idx_heads=wl.n_idx_heads, d_idx=wl.d_idx,
+        topk=wl.topk, window=wl.window, block_size=wl.block_size, cand_blocks=wl.cand_blocks,
+        ratio=wl.ratio, rope_theta=wl.rope_theta,
+    )
+
+
+def build_cache(inp, b: int, stop_pos: int, chunk: int = 1 << 14) -> csa2.SeqCache:
+    """Cache of sequence b holding every entry made from positions 0 .. stop_pos-1."""
+    wl = inp.wl
+    logits, w_ik = inp.pair_logits(), inp.w_ik()
+    cache = csa2.SeqCache(wl.kv, wl.main_group, wl.idx_group, {}, {})
+    chunk -= chunk % wl.ratio
+    for p0 in range(0, stop_pos, chunk):
+        p1 = min(stop_pos, p0 + chunk)
+        _, main_raw, _, idx_raw, _ = csa2.make_entries(
+            inp.latent(b, p0, p1), p0, logits, w_ik, wl.ratio, wl.d_rope, wl.rope_theta, wl.kv,
+            wl.main_group, wl.idx_group,
+        )
+        cache.append(main_raw, idx_raw)
+    return cache
+
+
+def layer_specs(inp, seqs) -> list:
+    """Per-layer oracle specs holding the query-side tensors of sequences ``seqs``."""
+    wl = inp.wl
+    specs = []
+    for li, plan in enumerate(wl.layers):
+        swa, swa_first = inp.swa(li)
+        specs.append(
+            csa2.LayerSpec(
+                mode=plan.mode, source=plan.source, make_pool=plan.make_pool,
+                q=inp.q(li)[seqs].astype(np.float64), q_idx=inp.q_idx(li)[seqs].astype(np.float64),
+                head_w=inp.head_w(li)[seqs].astype(np.float64), swa=swa[seqs].astype(np.float64),
+                swa_first=swa_first[seqs],
+            )
+        )
+    return specs
+
+
+def run_step(inp, seqs=None, caches=None):
+    """Oracle result of one step for sequences ``seqs`` (default: all).
+
+    ``caches`` may pass prebuilt prior caches (entries from positions
+    0 .. prior-1); the step's new entries are appended to copies of them.
+    Returns (per-layer results of csa2.run_group, caches after the step).
+    """
+    wl = inp.wl
+    seqs = list(range(wl.batch)) if seqs is None else list(seqs)
+    dims = dims_of(wl)
+    out_caches = []
+    for i, b in enumerate(seqs):
+        if caches is None:
+            cache = build_cache(inp, b, wl.prior)
+        else:
+            src = caches[i]
+            cache = csa2.SeqCache(src.kv_fmt, src.main_group, src.idx_group,
+                                  {k: v.copy() for k, v in src.main_raw.items()},
+                                  {k: v.copy() for k, v in src.idx_raw.items()})
+        if wl.new:
+            _, main_raw, _, idx_raw, _ = csa2.make_entries(
+                inp.latent(b, wl.prior, wl.context), wl.prior, inp.pair_logits(), inp.w_ik(), wl.ratio,
+                wl.d_rope, wl.rope_theta, wl.kv, wl.main_group, wl.idx_group,
+            )
+            cache.append(main_raw, idx_raw)
+        out_caches.append(cache)
+    q_pos = wl.q_positions()[seqs]
+    n_entries = [c.n_entries for c in out_caches]
+    results = csa2.run_group(dims, out_caches, n_entries, q_pos, layer_specs(inp, seqs))
+    return results, out_caches

@@ -1,0 +1,214 @@
+"""Seeded synthetic inputs for the CSA2 workloads.
+
+This module only draws random numbers and rounds them to the activation
+dtype; it holds none of the method's arithmetic.  Both the oracle-side tests
+and the GPU side consume exactly the arrays it returns.
+
+Every tensor gets its own PCG64 stream, keyed by (seed, workload, tensor,
+layer, sequence, chunk), so a test can regenerate one sequence or one chunk
+of a long latent without drawing the rest.
+
+Distributions (one reading of the workload descriptions):
+latent, queries, indexer queries, head weights, compressor logits and window
+rows are N(0, 1); the indexer-K projection W_ik is N(0, 1/d) (standard
+deviation 1/sqrt(fan_in)).
+"""
+from __future__ import annotations
+
+import zlib
+from dataclasses import dataclass, field, replace
+
+import numpy as np
+
+CHUNK = 4096  # latent rows per generated chunk
+
+
+@dataclass(frozen=True)
+class LayerPlan:
+    mode: str  # "full" | "reindex" | "reuse"
+    source: int = -1
+    make_pool: bool = False
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    ratio: int
+    d: int
+    d_rope: int
+    n_heads: int
+    n_idx_heads: int
+    d_idx: int
+    topk: int
+    window: int
+    act: str  # activation dtype: "f32" | "bf16"
+    kv: str  # cache dtype: "f32" | "bf16" | "fp4"
+    prior: int  # latent positions already compressed into the cache
+    new: int  # latent positions compressed by the step itself
+    n_q: int  # queries per sequence, at the last n_q positions
+    layers: tuple = (LayerPlan("full"),)
+    block_size: int = 8
+    cand_blocks: int = 2048
+    main_group: int = 32
+    idx_group: int = 32
+    rope_theta: float = 10000.0
+    description: str = ""
+
+    @property
+    def context(self) -> int:
+        return self.prior + self.new
+
+    @property
+    def capacity(self) -> int:
+        return self.context // self.ratio
+
+    @property
+    def n_prior_entries(self) -> int:
+        return self.prior // self.ratio
+
+    def q_positions(self) -> np.ndarray:
+        t = np.arange(self.context - self.n_q, self.context, dtype=np.int32)
+        return np.broadcast_to(t, (self.batch, self.n_q)).copy()
+
+    def swa_span(self) -> tuple[int, int]:
+        """First window position needed and number of window rows per sequence."""
+        t0 = self.context - self.n_q
+        first = max(0, t0 - self.window + 1)
+        return first, self.context - first
+
+
+_PROD = dict(d=512, d_rope=64, n_heads=64, n_idx_heads=32, d_idx=128, topk=512, window=128)
+
+WORKLOADS = {
+    # The five workloads the measurements are quoted on.
+    "tiny_encoder": Workload(
+        "tiny_encoder", batch=1, ratio=2, d=64, d_rope=16, n_heads=8, n_idx_heads=4, d_idx=32,
+        topk=64, window=16, act="f32", kv="f32", prior=1008, new=16, n_q=16,
+        description="tiny encoder layer, fp32: 1024 positions at ratio 2 (512 entries), "
+        "causal decode of the last 16 queries",
+    ),
+    "decode_32k": Workload(
+        "decode_32k", batch=16, ratio=1, **_PROD, act="bf16", kv="bf16", prior=32767, new=1, n_q=1,
+        description="decoder-layer decode, bf16: 16 sequences x 32768 context, ratio 1, Full",
+    ),
+    "prefill_128k": Workload(
+        "prefill_128k", batch=1, ratio=2, **_PROD, act="bf16", kv="bf16", prior=131072, new=4096, n_q=4096,
+        description="encoder chunked prefill, bf16: 131072 prior positions at ratio 2, "
+        "a chunk of 4096 causal queries",
+    ),
+    "group_256k": Workload(
+        "group_256k", batch=4, ratio=1, **_PROD, act="bf16", kv="bf16", prior=262143, new=1, n_q=1,
+        layers=(LayerPlan("full", make_pool=True), LayerPlan("reindex", 0), LayerPlan("reindex", 0),
+                LayerPlan("reuse", 2)),
+        description="cross-layer group decode, bf16: 4 x 262144, Full + Reindex + Reindex + Reuse(3rd)",
+    ),
+    "fp4_1m": Workload(
+        "fp4_1m", batch=2, ratio=1, **_PROD, act="bf16", kv="fp4", prior=1048575, new=1, n_q=1,
+        layers=(LayerPlan("full", make_pool=True),), main_group=32, idx_group=32,
+        description="long-context decode with FP4 KV (E2M1, one E4M3 scale per 32): 2 x 1048576, HSI",
+    ),
+}
+
+# Smaller cases of the same shapes, for parity at sizes the oracle finishes in seconds.
+SMALL = {
+    "tiny_bf16": replace(WORKLOADS["tiny_encoder"], name="tiny_bf16", act="bf16", kv="bf16"),
+    "tiny_fp4": replace(WORKLOADS["tiny_encoder"], name="tiny_fp4", act="bf16", kv="fp4"),
+    "decode_small": replace(WORKLOADS["decode_32k"], name="decode_small", batch=3, prior=3000, new=1),
+    "decode_dense": replace(WORKLOADS["decode_32k"], name="decode_dense", batch=2, prior=400, new=1),
+    "hsi_small": replace(
+        WORKLOADS["decode_32k"], name="hsi_small", batch=2, prior=9000, new=1, topk=128, cand_blocks=64,
+        layers=(LayerPlan("full", make_pool=True), LayerPlan("reindex", 0), LayerPlan("reuse", 1)),
+    ),
+    "group_small": replace(WORKLOADS["group_256k"], name="group_small", batch=2, prior=20000, new=1),
+    "fp4_small": replace(WORKLOADS["fp4_1m"], name="fp4_small", batch=2, prior=20000, new=1),
+    "fp4_pages": replace(WORKLOADS["fp4_1m"], name="fp4_pages", batch=2, prior=5000, new=1, main_group=16),
+    "prefill_small": replace(WORKLOADS["prefill_128k"], name="prefill_small", prior=4096, new=512, n_q=512),
+    "multi_q_small": replace(WORKLOADS["decode_32k"], name="multi_q_small", batch=2, prior=2990, new=10, n_q=10),
+}
+
+ALL = {**WORKLOADS, **SMALL}
+
+
+def _key(*parts) -> list:
+    out = []
+    for p in parts:
+        out.append(zlib.crc32(p.encode()) if isinstance(p, str) else int(p))
+    return out
+
+
+def round_act(x: np.ndarray, act: str) -> np.ndarray:
+    """float32 array whose values are representable in the activation dtype.
+
+    bf16: round to nearest even on the float32 bit pattern (inputs only).
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if act == "f32":
+        return x
+    if act != "bf16":
+        raise ValueError(act)
+    u = x.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000).astype(np.uint32)
+    return r.view(np.float32)
+
+
+class Inputs:
+    """All synthetic tensors of one workload (float32 arrays, values exact in the act dtype)."""
+
+    def __init__(self, wl: Workload, seed: int = 0):
+        self.wl = wl
+        self.seed = seed
+
+    def _rng(self, *parts) -> np.random.Generator:
+        ss = np.random.SeedSequence(_key(self.seed, self.wl.name, *parts))
+        return np.random.Generator(np.random.PCG64(ss))
+
+    def _normal(self, shape, std, *parts) -> np.ndarray:
+        x = self._rng(*parts).standard_normal(shape, dtype=np.float32)
+        if std != 1.0:
+            x *= np.float32(std)
+        return x
+
+    # ---- cache-side tensors -------------------------------------------------
+    def latent(self, b: int, start: int, stop: int) -> np.ndarray:
+        """Latent rows of sequence b at positions start .. stop-1, [stop-start, d]."""
+        d = self.wl.d
+        out = np.empty((max(0, stop - start), d), dtype=np.float32)
+        c0, c1 = start // CHUNK, (stop - 1) // CHUNK if stop > start else start // CHUNK - 1
+        for c in range(c0, c1 + 1):
+            chunk = round_act(self._normal((CHUNK, d), 1.0, "latent", b, c), self.wl.act)
+            lo, hi = max(start, c * CHUNK), min(stop, (c + 1) * CHUNK)
+            out[lo - start : hi - start] = chunk[lo - c * CHUNK : hi - c * CHUNK]
+        return out
+
+    def pair_logits(self) -> np.ndarray | None:
+        if self.wl.ratio == 1:
+            return None
+        return self._normal((self.wl.ratio, self.wl.d), 1.0, "pair_logits")
+
+    def w_ik(self) -> np.ndarray:
+        wl = self.wl
+        return round_act(self._normal((wl.d, wl.d_idx), 1.0 / np.sqrt(wl.d), "w_ik"), wl.act)
+
+    # ---- per-layer query-side tensors ----------------------------------------
+    def q(self, layer: int) -> np.ndarray:
+        wl = self.wl
+        return round_act(self._normal((wl.batch, wl.n_q, wl.n_heads, wl.d), 1.0, "q", layer), wl.act)
+
+    def q_idx(self, layer: int) -> np.ndarray:
+        wl = self.wl
+        return round_act(self._normal((wl.batch, wl.n_q, wl.n_idx_heads, wl.d_idx), 1.0, "q_idx", layer), wl.act)
+
+    def head_w(self, layer: int) -> np.ndarray:
+        wl = self.wl
+        return self._normal((wl.batch, wl.n_q, wl.n_idx_heads), 1.0, "head_w", layer)
+
+    def swa(self, layer: int) -> tuple[np.ndarray, np.ndarray]:
+        wl = self.wl
+        first, n = wl.swa_span()
+        rows = round_act(self._normal((wl.batch, n, wl.d), 1.0, "swa", layer), wl.act)
+        return rows, np.full(wl.batch, first, dtype=np.int32)
+
+
+def get(name: str) -> Workload:
+    return ALL[name]
