@@ -1,0 +1,268 @@
+/*
+ * csa2.h - C ABI of the CSA2 sparse-attention hot path on AMD MI355X (gfx950).
+ *
+ * CSA2 is the compressed sparse attention of the DeepSeek-V4.1-Flash technical
+ * report as described on the web pages this library follows:
+ *   [ZB]   zartbot's walkthrough of the report (hn.213312.xyz), sections 1-3;
+ *   [ELPH] elph.ru, "DeepSeek-V4.1 Flash: Squeezing the KV Cache Fourfold for
+ *          Long Context";
+ *   [36KR] eu.36kr.com, "What 'black technologies' does DeepSeek V4.1 Flash
+ *          adopt?".
+ * A layer keeps one shared latent main KV (512 channels, 64 of them rotary)
+ * and an indexer K projected from it; a lightweight indexer scores the
+ * entries, a top-k picks 512 of them (optionally through the hierarchical
+ * sparse indexer's block pool), and attention runs over the picked rows
+ * concatenated with a 128-row sliding window.  Layers share caches in Full,
+ * Reindex or Reuse mode.
+ *
+ * Conventions for every entry point:
+ *  - All array arguments are DEVICE pointers unless stated otherwise; the
+ *    caller owns every buffer (inputs, outputs, caches, workspace).  The
+ *    library allocates nothing on a call path and keeps no pointer after the
+ *    call returns.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *    default stream).  Results are valid after the caller synchronises.
+ *  - Every argument that the host can check is checked before any HIP call;
+ *    a failing check returns a negative csa2_status and enqueues nothing.
+ *    Values that live on the device (positions, entry counts, indices) are
+ *    clamped or skipped by the kernels, never trusted for addressing.
+ *  - Errors from a kernel that faults surface at the caller's next
+ *    synchronisation, as with any HIP work.
+ *  - No C++ exception crosses this boundary.  csa2_last_error() returns a
+ *    message for the failing call (cleared when a call starts).
+ *  - Calls on different streams with different outputs and workspaces may
+ *    run concurrently.
+ *
+ * Layouts are row-major, innermost index last.  "act" is the activation
+ * element type of csa2_dims.act_dtype (float32 or bfloat16 bit patterns).
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA2_ABI_VERSION 1
+
+typedef enum csa2_status {
+  CSA2_OK = 0,
+  CSA2_ERR_INVALID_ARG = -1, /* NULL where required, non-positive or inconsistent sizes, misalignment */
+  CSA2_ERR_UNSUPPORTED = -2, /* dtype, ratio, mode or shape the kernels do not implement */
+  CSA2_ERR_WORKSPACE = -3,   /* workspace missing or smaller than csa2_workspace_size() */
+  CSA2_ERR_MODE_ORDER = -4,  /* Reindex/Reuse source is not a suitable earlier layer */
+  CSA2_ERR_HIP = -5          /* a HIP runtime call or kernel launch failed */
+} csa2_status;
+
+typedef enum csa2_dtype {
+  CSA2_F32 = 0,  /* IEEE float32 */
+  CSA2_BF16 = 1, /* bfloat16 bit patterns (uint16) */
+  CSA2_FP4 = 2   /* cache only: E2M1 codes, two per byte (even channel in the low
+                    nibble), plus one E4M3 (FN) scale byte per group of channels */
+} csa2_dtype;
+
+typedef enum csa2_mode {
+  CSA2_FULL = 0,    /* score all visible entries, write the top-k (and the HSI pool) */
+  CSA2_REINDEX = 1, /* rescore the shared indexer K with the layer's own indexer Q */
+  CSA2_REUSE = 2    /* read an earlier layer's top-k; never touches indexer K */
+} csa2_mode;
+
+typedef enum csa2_entry_point {
+  CSA2_EP_COMPRESS = 0,
+  CSA2_EP_INDEX_TOPK = 1,
+  CSA2_EP_SPARSE_ATTN = 2,
+  CSA2_EP_LAYER_GROUP = 3
+} csa2_entry_point;
+
+/* Shape of one CSA2 layer ([ZB] section 1.2 hyper-parameters). */
+typedef struct csa2_dims {
+  int32_t d;           /* latent width = query head width (512); multiple of 32 */
+  int32_t d_rope;      /* trailing rotary channels of the latent (64); even, <= d */
+  int32_t n_heads;     /* main query heads (64) */
+  int32_t n_idx_heads; /* indexer heads (32) */
+  int32_t d_idx;       /* indexer head width = indexer-K width (128); multiple of 32 */
+  int32_t topk;        /* entries kept per query (512); 1..2048 */
+  int32_t window;      /* sliding-window rows per query (128); >= 0 */
+  int32_t block_size;  /* HSI block size (8); must be 8 */
+  int32_t cand_blocks; /* HSI pool size in blocks (2048); 1..2048 */
+  int32_t act_dtype;   /* CSA2_F32 or CSA2_BF16 for latent, W_ik, q, idx_q, window rows, out */
+  double rope_theta;   /* RoPE base (10000) */
+} csa2_dims;
+
+/* The shared caches of one layer group: main KV and indexer K.
+ *
+ * Entry j of sequence b is the merge of latent positions ratio*j ..
+ * ratio*j+ratio-1, rotated at position ratio*j+ratio-1 ([ZB] 2.3.1, 2.4.4).
+ * It is visible to a query at position t iff ratio*j + ratio - 1 <= t and
+ * j < n_entries[b].
+ *
+ *  F32 / BF16:  main  [batch][capacity][d]      act-sized elements of kv_dtype
+ *               idx_k [batch][capacity][d_idx]
+ *  FP4:         main  [batch][capacity][d/2]     bytes (E2M1 codes)
+ *               main_scale [batch][capacity][d/main_group]     E4M3 bytes
+ *               idx_k [batch][capacity][d_idx/2] bytes
+ *               idx_scale  [batch][capacity][d_idx/idx_group]  E4M3 bytes
+ * All base pointers must be 16-byte aligned.
+ */
+typedef struct csa2_kv_cache {
+  int32_t kv_dtype;   /* CSA2_F32, CSA2_BF16 or CSA2_FP4 */
+  int32_t ratio;      /* compress ratio the entries were made with: 1 or 2 */
+  int32_t main_group; /* FP4: channels per scale in main KV: 16 or 32 ([ZB] 2.4.4 says 16) */
+  int32_t idx_group;  /* FP4: channels per scale in indexer K: 16 or 32 */
+  int32_t batch;      /* sequences */
+  int32_t reserved0;  /* must be 0 */
+  int64_t capacity;   /* entry slots per sequence; 1 .. 1048576 */
+  void* main;
+  uint8_t* main_scale;     /* FP4 only, else NULL */
+  void* idx_k;             /* may be NULL for calls that never read it (Reuse attention) */
+  uint8_t* idx_scale;      /* FP4 only, else NULL */
+  const int32_t* n_entries; /* device [batch]; values are clamped to [0, capacity] */
+} csa2_kv_cache;
+
+/* csa2_compress - write new cache entries from latent rows (path step a1/a2/a7).
+ *
+ * [ZB] 2.3.1: ratio-2 layers merge two adjacent positions into one entry
+ * with per-channel learned weights, ratio-1 layers keep one entry per
+ * position, and the indexer K is projected from the main KV.  For each
+ * sequence b and m in 0 .. n_pos/ratio-1, entry j = first_pos[b]/ratio + m:
+ *   e[c]   = sum_i softmax_i(pair_logits[:, c]) * latent[b][ratio*m + i][c]
+ *   e_hat  = e with its last d_rope channels rotated at position ratio*j+ratio-1
+ *   main[j]  = store(e_hat)                 (round to nearest even / FP4 codec)
+ *   idx_k[j] = store(e_hat . W_ik)          (from the unrounded e_hat)
+ * The merge, rotation and projection run in float64, so the stored bits are
+ * the single rounding of the exact value.
+ *
+ *  latent      [batch][n_pos][d] act
+ *  first_pos   device [batch]: position of latent row 0; a multiple of ratio
+ *  n_pos       rows per sequence; a positive multiple of cache->ratio
+ *  pair_logits device [ratio][d] float32; NULL iff ratio == 1
+ *  w_ik        device [d][d_idx] act
+ * Entries that fall outside [0, capacity) are not written.  n_entries is
+ * not updated: the caller owns it.
+ */
+int csa2_compress(const csa2_dims* dims, const csa2_kv_cache* cache, const void* latent,
+                  const int32_t* first_pos, int32_t n_pos, const float* pair_logits, const void* w_ik,
+                  void* stream);
+
+/* csa2_index_topk - indexer scores and top-k selection (path steps a3/a4).
+ *
+ * Score of entry j for query (b, t) ([ZB] 2.3.1 lightweight indexer):
+ *   s_j = sum_h head_w[h] * max(0, idx_q[h] . K_j)
+ * over the domain: every visible entry (pool_in == NULL), or the visible
+ * entries of the blocks listed in pool_in (Reindex, [ZB] 2.3.4).  The top-k
+ * keeps the topk highest scores, ties to the lower entry id, and is written
+ * in ascending entry id, padded with -1.
+ * With pool_out != NULL the HSI pool is also built ([ZB] 2.3.4): the
+ * per-block maximum of the full scores over aligned blocks of block_size,
+ * the block of the newest visible entry forced in, then the best blocks up
+ * to cand_blocks (ties to the lower block), written ascending, padded -1.
+ *
+ *  idx_q     [batch][n_q][n_idx_heads][d_idx] act
+ *  head_w    [batch][n_q][n_idx_heads] float32
+ *  q_pos     [batch][n_q] int32 token positions (>= 0)
+ *  pool_in   NULL or [batch][n_q][cand_blocks] int32 block ids
+ *  topk_out  [batch][n_q][topk] int32
+ *  pool_out  NULL or [batch][n_q][cand_blocks] int32 (not allowed with pool_in)
+ *  topk_scores NULL or [batch][n_q][topk] float32: score of each kept entry
+ *  ws        workspace of at least csa2_workspace_size(..., CSA2_EP_INDEX_TOPK, n_q) bytes,
+ *            256-byte aligned
+ */
+int csa2_index_topk(const csa2_dims* dims, const csa2_kv_cache* cache, const void* idx_q,
+                    const float* head_w, const int32_t* q_pos, int32_t n_q, const int32_t* pool_in,
+                    int32_t* topk_out, int32_t* pool_out, float* topk_scores, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/* csa2_sparse_attn - attention over the kept entries plus the window (path step a5).
+ *
+ * [ZB] 2.2.2: global (sparse) KV and local (window) KV are concatenated and
+ * scored together with Q; [ZB] 3.3.1: key equals value.  For query (b, t)
+ * and head h, with q_hat = q rotated at t on its last d_rope channels:
+ *   rows  = [main[j] for j in topk (j >= 0)] ++ [swa row of p for p in
+ *            max(0, t-window+1) .. t that lies in the window buffer]
+ *   out_h = softmax(q_hat . rows^T / sqrt(d)) . rows,  lse_h = log(sum exp(.))
+ *
+ *  q             [batch][n_q][n_heads][d] act (not rotated)
+ *  q_pos         [batch][n_q] int32
+ *  topk          [batch][n_q][topk] int32 entry ids or -1
+ *  swa_kv        [batch][n_swa][d] act, rows already rotated
+ *  swa_first_pos [batch] int32: position of window-buffer row 0
+ *  out           [batch][n_q][n_heads][d] act
+ *  lse           NULL or [batch][n_q][n_heads] float32 (natural log)
+ *  ws            at least csa2_workspace_size(..., CSA2_EP_SPARSE_ATTN, n_q) bytes
+ * cache->idx_k may be NULL.
+ */
+int csa2_sparse_attn(const csa2_dims* dims, const csa2_kv_cache* cache, const void* q,
+                     const int32_t* q_pos, int32_t n_q, const int32_t* topk, const void* swa_kv,
+                     const int32_t* swa_first_pos, int32_t n_swa, void* out, float* lse, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* One layer of a csa2_layer_group call ([ZB] 2.3.2, 3.2 access table). */
+typedef struct csa2_layer {
+  int32_t mode;      /* csa2_mode */
+  int32_t source;    /* REINDEX: earlier FULL layer (with make_pool) whose pool is searched,
+                        or -1 to search every visible entry; REUSE: earlier FULL or REINDEX
+                        layer whose top-k is read; FULL: must be -1 */
+  int32_t make_pool; /* FULL: nonzero builds the HSI pool into `pool` */
+  int32_t n_swa;     /* window-buffer rows */
+  const void* q;     /* [batch][n_q][n_heads][d] act */
+  const void* idx_q; /* FULL/REINDEX: [batch][n_q][n_idx_heads][d_idx] act; REUSE: NULL */
+  const float* head_w; /* FULL/REINDEX: [batch][n_q][n_idx_heads]; REUSE: NULL */
+  const void* swa_kv;  /* [batch][n_swa][d] act */
+  const int32_t* swa_first_pos; /* [batch] */
+  void* out;         /* [batch][n_q][n_heads][d] act */
+  float* lse;        /* NULL or [batch][n_q][n_heads] */
+  int32_t* topk;     /* FULL/REINDEX: written, [batch][n_q][topk]; REUSE: NULL, or receives
+                        a copy of the source's top-k */
+  int32_t* pool;     /* FULL with make_pool: written, [batch][n_q][cand_blocks]; else NULL */
+} csa2_layer;
+
+/* New latent rows to compress before the group runs (Full-mode cache write). */
+typedef struct csa2_compress_args {
+  const void* latent;
+  const int32_t* first_pos;
+  int32_t n_pos;
+  int32_t reserved0; /* must be 0 */
+  const float* pair_logits;
+  const void* w_ik;
+} csa2_compress_args;
+
+/* csa2_layer_group - run layers that share one main KV and indexer K (path step a6).
+ *
+ * Layers run in order on `stream`.  If `compress` is non-NULL its rows are
+ * written into the cache first (csa2_compress).  Full layers score every
+ * visible entry; Reindex layers rescore the pool of their source (or every
+ * visible entry) with their own indexer Q; Reuse layers attend with their
+ * source's top-k.  Reindex and Reuse never write the caches and Reuse
+ * never reads the indexer K ([ZB] 3.2).  Sources must be earlier layers:
+ * reuse flows only from earlier to later layers ([ZB] 3.3.1).
+ *  q_pos  [batch][n_q] int32, shared by all layers
+ *  ws     at least csa2_workspace_size(..., CSA2_EP_LAYER_GROUP, n_q) bytes
+ */
+int csa2_layer_group(const csa2_dims* dims, const csa2_kv_cache* cache, int32_t n_layers,
+                     const csa2_layer* layers, const int32_t* q_pos, int32_t n_q,
+                     const csa2_compress_args* compress, void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of workspace an entry point needs for n_q queries per sequence, or 0
+ * if the arguments are invalid (csa2_last_error() then says why).  Sized
+ * from cache->capacity and cache->batch. */
+size_t csa2_workspace_size(const csa2_dims* dims, const csa2_kv_cache* cache, int32_t entry_point,
+                           int32_t n_q);
+
+/* Static string naming a csa2_status. */
+const char* csa2_status_str(int status);
+
+/* Message of the last failing call on this thread; every entry point clears it
+ * on entry, so it is "" after a call that succeeded. */
+const char* csa2_last_error(void);
+
+/* CSA2_ABI_VERSION of the loaded library. */
+int32_t csa2_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA2_H */

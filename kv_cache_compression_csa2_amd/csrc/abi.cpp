@@ -1,0 +1,359 @@
+// C ABI of the CSA2 hot path: argument validation, workspace carving and the
+// launch sequence of every entry point.  Every check runs on the host before
+// any HIP call; no exception leaves this file.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "csa2.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int fail_hip(hipError_t e, const char* where) {
+  return fail(CSA2_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxCapacity = int64_t(1) << 20;
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int check_dims(const csa2_dims* d) {
+  if (!d) return fail(CSA2_ERR_INVALID_ARG, "dims is NULL");
+  if (d->d <= 0 || d->d % 32 || d->d > 1024) return fail(CSA2_ERR_UNSUPPORTED, "d=%d: need a multiple of 32 in [32, 1024]", d->d);
+  if (d->d_rope < 0 || d->d_rope % 2 || d->d_rope > d->d) return fail(CSA2_ERR_INVALID_ARG, "d_rope=%d: need even, 0..d", d->d_rope);
+  if (d->n_heads <= 0 || d->n_heads > 1024) return fail(CSA2_ERR_INVALID_ARG, "n_heads=%d out of range", d->n_heads);
+  if (d->n_idx_heads <= 0 || d->d_idx <= 0 || d->d_idx % 32 || d->d_idx > 512)
+    return fail(CSA2_ERR_UNSUPPORTED, "indexer heads %d x %d: need width a multiple of 32 up to 512", d->n_idx_heads, d->d_idx);
+  if (int64_t(d->n_idx_heads) * d->d_idx > 8192)
+    return fail(CSA2_ERR_UNSUPPORTED, "indexer query of %d x %d exceeds 8192 elements", d->n_idx_heads, d->d_idx);
+  if (d->topk < 1 || d->topk > 2048) return fail(CSA2_ERR_UNSUPPORTED, "topk=%d: need 1..2048", d->topk);
+  if (d->window < 0 || d->window > 4096) return fail(CSA2_ERR_UNSUPPORTED, "window=%d: need 0..4096", d->window);
+  if (d->block_size != 8) return fail(CSA2_ERR_UNSUPPORTED, "block_size=%d: only 8 is implemented", d->block_size);
+  if (d->cand_blocks < 1 || d->cand_blocks > 2048) return fail(CSA2_ERR_UNSUPPORTED, "cand_blocks=%d: need 1..2048", d->cand_blocks);
+  if (d->act_dtype != CSA2_F32 && d->act_dtype != CSA2_BF16) return fail(CSA2_ERR_UNSUPPORTED, "act_dtype=%d", d->act_dtype);
+  if (!(d->rope_theta > 0.0)) return fail(CSA2_ERR_INVALID_ARG, "rope_theta must be positive");
+  return CSA2_OK;
+}
+
+// need_idx: the call reads or writes the indexer K.
+int check_cache(const csa2_dims* d, const csa2_kv_cache* c, bool need_idx) {
+  if (!c) return fail(CSA2_ERR_INVALID_ARG, "cache is NULL");
+  if (c->kv_dtype != CSA2_F32 && c->kv_dtype != CSA2_BF16 && c->kv_dtype != CSA2_FP4)
+    return fail(CSA2_ERR_UNSUPPORTED, "kv_dtype=%d", c->kv_dtype);
+  if (c->ratio != 1 && c->ratio != 2) return fail(CSA2_ERR_UNSUPPORTED, "ratio=%d: need 1 or 2", c->ratio);
+  if (c->batch <= 0 || c->batch > 65535) return fail(CSA2_ERR_INVALID_ARG, "batch=%d out of range", c->batch);
+  if (c->reserved0 != 0) return fail(CSA2_ERR_INVALID_ARG, "cache reserved field must be 0");
+  if (c->capacity <= 0 || c->capacity > kMaxCapacity)
+    return fail(CSA2_ERR_UNSUPPORTED, "capacity=%lld: need 1..%lld", (long long)c->capacity, (long long)kMaxCapacity);
+  if (!c->main || !c->n_entries) return fail(CSA2_ERR_INVALID_ARG, "cache main or n_entries is NULL");
+  if (!aligned16(c->main)) return fail(CSA2_ERR_INVALID_ARG, "cache main is not 16-byte aligned");
+  if (need_idx && !c->idx_k) return fail(CSA2_ERR_INVALID_ARG, "cache idx_k is NULL but this call needs the indexer K");
+  if (c->idx_k && !aligned16(c->idx_k)) return fail(CSA2_ERR_INVALID_ARG, "cache idx_k is not 16-byte aligned");
+  if (c->kv_dtype == CSA2_FP4) {
+    if (c->main_group != 16 && c->main_group != 32) return fail(CSA2_ERR_UNSUPPORTED, "main_group=%d: need 16 or 32", c->main_group);
+    if (c->idx_group != 16 && c->idx_group != 32) return fail(CSA2_ERR_UNSUPPORTED, "idx_group=%d: need 16 or 32", c->idx_group);
+    if (d->d % c->main_group || d->d_idx % c->idx_group) return fail(CSA2_ERR_INVALID_ARG, "widths must be multiples of the FP4 groups");
+    if (!c->main_scale) return fail(CSA2_ERR_INVALID_ARG, "FP4 cache needs main_scale");
+    if (need_idx && !c->idx_scale) return fail(CSA2_ERR_INVALID_ARG, "FP4 cache needs idx_scale");
+  }
+  return CSA2_OK;
+}
+
+int check_ptr(const void* p, const char* name) {
+  if (!p) return fail(CSA2_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(CSA2_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return CSA2_OK;
+}
+
+int64_t dom_cap_flat(const csa2_kv_cache* c) { return int64_t(round_up(size_t(c->capacity), 256)); }
+int64_t dom_cap_pool(const csa2_dims* d) { return int64_t(round_up(size_t(d->cand_blocks) * 8, 256)); }
+
+size_t index_ws_bytes(const csa2_dims* d, const csa2_kv_cache* c, int32_t n_q) {
+  const int64_t cap = dom_cap_flat(c) > dom_cap_pool(d) ? dom_cap_flat(c) : dom_cap_pool(d);
+  const size_t rows = size_t(c->batch) * size_t(n_q);
+  return round_up(rows * cap * 4, kAlign) + round_up(rows * (cap / 8) * 4, kAlign) + round_up(rows * (cap / 64) * 4, kAlign);
+}
+
+csa2::ScanScratch carve_index(void* ws, const csa2_dims* d, const csa2_kv_cache* c, int32_t n_q, bool pool_domain) {
+  const int64_t cap = dom_cap_flat(c) > dom_cap_pool(d) ? dom_cap_flat(c) : dom_cap_pool(d);
+  const size_t rows = size_t(c->batch) * size_t(n_q);
+  csa2::ScanScratch s;
+  char* p = static_cast<char*>(ws);
+  s.dom_cap = pool_domain ? dom_cap_pool(d) : dom_cap_flat(c);
+  s.scores = reinterpret_cast<float*>(p);
+  p += round_up(rows * cap * 4, kAlign);
+  s.bmax = reinterpret_cast<float*>(p);
+  p += round_up(rows * (cap / 8) * 4, kAlign);
+  s.sbmax = reinterpret_cast<float*>(p);
+  return s;
+}
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return CSA2_OK;
+  if (!ws) return fail(CSA2_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", need);
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return fail(CSA2_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (ws_bytes < need) return fail(CSA2_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, need);
+  return CSA2_OK;
+}
+
+int check_compress(const csa2_dims* d, const csa2_kv_cache* c, const void* latent, const int32_t* first_pos,
+                   int32_t n_pos, const float* pair_logits, const void* w_ik) {
+  int st;
+  if ((st = check_ptr(latent, "latent")) || (st = check_ptr(first_pos, "first_pos")) || (st = check_ptr(w_ik, "w_ik")))
+    return st;
+  if (n_pos <= 0 || n_pos % c->ratio) return fail(CSA2_ERR_INVALID_ARG, "n_pos=%d: need a positive multiple of ratio %d", n_pos, c->ratio);
+  if (n_pos / c->ratio > 65535) return fail(CSA2_ERR_UNSUPPORTED, "n_pos=%d: at most 65535 entries per call", n_pos);
+  if ((c->ratio == 1) != (pair_logits == nullptr)) return fail(CSA2_ERR_INVALID_ARG, "pair_logits must be NULL iff ratio == 1");
+  if (pair_logits && !aligned16(pair_logits)) return fail(CSA2_ERR_INVALID_ARG, "pair_logits is not 16-byte aligned");
+  return CSA2_OK;
+}
+
+// hipGetLastError() is per thread and sticky across unrelated runtime calls
+// (another library's probe may have left an error behind); clear it so that
+// the check after our launches reports only our launches.
+void clear_stale_error() { (void)hipGetLastError(); }
+
+int run_compress(const csa2_dims* d, const csa2_kv_cache* c, const void* latent, const int32_t* first_pos,
+                 int32_t n_pos, const float* pair_logits, const void* w_ik, hipStream_t s) {
+  clear_stale_error();
+  hipError_t e = csa2::launch_compress(*d, *c, latent, first_pos, n_pos, pair_logits, w_ik, s);
+  return e == hipSuccess ? CSA2_OK : fail_hip(e, "compress launch");
+}
+
+int run_index(const csa2_dims* d, const csa2_kv_cache* c, const void* idx_q, const float* head_w,
+              const int32_t* q_pos, int32_t n_q, const int32_t* pool_in, int32_t* topk_out, int32_t* pool_out,
+              float* topk_scores, void* ws, hipStream_t s) {
+  const csa2::ScanScratch ss = carve_index(ws, d, c, n_q, pool_in != nullptr);
+  clear_stale_error();
+  hipError_t e = csa2::launch_scan(*d, *c, idx_q, head_w, q_pos, n_q, pool_in, ss, s);
+  if (e != hipSuccess) return fail_hip(e, "index scan launch");
+  e = csa2::launch_select(*d, *c, q_pos, n_q, pool_in, ss, topk_out, pool_out, topk_scores, s);
+  if (e != hipSuccess) return fail_hip(e, "top-k select launch");
+  return CSA2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t csa2_abi_version(void) { return CSA2_ABI_VERSION; }
+
+const char* csa2_last_error(void) { return g_last_error.c_str(); }
+
+const char* csa2_status_str(int status) {
+  switch (status) {
+    case CSA2_OK: return "CSA2_OK";
+    case CSA2_ERR_INVALID_ARG: return "CSA2_ERR_INVALID_ARG";
+    case CSA2_ERR_UNSUPPORTED: return "CSA2_ERR_UNSUPPORTED";
+    case CSA2_ERR_WORKSPACE: return "CSA2_ERR_WORKSPACE";
+    case CSA2_ERR_MODE_ORDER: return "CSA2_ERR_MODE_ORDER";
+    case CSA2_ERR_HIP: return "CSA2_ERR_HIP";
+    default: return "CSA2_ERR_UNKNOWN";
+  }
+}
+
+size_t csa2_workspace_size(const csa2_dims* dims, const csa2_kv_cache* cache, int32_t entry_point, int32_t n_q) {
+  g_last_error.clear();
+  try {
+    if (check_dims(dims) || check_cache(dims, cache, false)) return 0;
+    if (n_q <= 0) {
+      fail(CSA2_ERR_INVALID_ARG, "n_q=%d must be positive", n_q);
+      return 0;
+    }
+    switch (entry_point) {
+      case CSA2_EP_COMPRESS: return 0;
+      case CSA2_EP_INDEX_TOPK: return index_ws_bytes(dims, cache, n_q);
+      case CSA2_EP_SPARSE_ATTN: return csa2::attn_workspace_bytes(*dims, *cache, n_q);
+      case CSA2_EP_LAYER_GROUP:
+        return round_up(index_ws_bytes(dims, cache, n_q), kAlign) + csa2::attn_workspace_bytes(*dims, *cache, n_q);
+      default:
+        fail(CSA2_ERR_INVALID_ARG, "entry_point=%d unknown", entry_point);
+        return 0;
+    }
+  } catch (...) {
+    fail(CSA2_ERR_HIP, "internal exception");
+    return 0;
+  }
+}
+
+int csa2_compress(const csa2_dims* dims, const csa2_kv_cache* cache, const void* latent, const int32_t* first_pos,
+                  int32_t n_pos, const float* pair_logits, const void* w_ik, void* stream) {
+  g_last_error.clear();
+  try {
+    int st;
+    if ((st = check_dims(dims)) || (st = check_cache(dims, cache, true))) return st;
+    if ((st = check_compress(dims, cache, latent, first_pos, n_pos, pair_logits, w_ik))) return st;
+    return run_compress(dims, cache, latent, first_pos, n_pos, pair_logits, w_ik, static_cast<hipStream_t>(stream));
+  } catch (...) {
+    return fail(CSA2_ERR_HIP, "internal exception");
+  }
+}
+
+int csa2_index_topk(const csa2_dims* dims, const csa2_kv_cache* cache, const void* idx_q, const float* head_w,
+                    const int32_t* q_pos, int32_t n_q, const int32_t* pool_in, int32_t* topk_out, int32_t* pool_out,
+                    float* topk_scores, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  try {
+    int st;
+    if ((st = check_dims(dims)) || (st = check_cache(dims, cache, true))) return st;
+    if (n_q <= 0 || n_q > 65535) return fail(CSA2_ERR_INVALID_ARG, "n_q=%d out of range", n_q);
+    if ((st = check_ptr(idx_q, "idx_q")) || (st = check_ptr(head_w, "head_w")) || (st = check_ptr(q_pos, "q_pos")) ||
+        (st = check_ptr(topk_out, "topk_out")))
+      return st;
+    if (pool_in && pool_out) return fail(CSA2_ERR_INVALID_ARG, "pool_in and pool_out are exclusive");
+    if (pool_in && !aligned16(pool_in)) return fail(CSA2_ERR_INVALID_ARG, "pool_in is not 16-byte aligned");
+    if (pool_out && !aligned16(pool_out)) return fail(CSA2_ERR_INVALID_ARG, "pool_out is not 16-byte aligned");
+    if (topk_scores && !aligned16(topk_scores)) return fail(CSA2_ERR_INVALID_ARG, "topk_scores is not 16-byte aligned");
+    if ((st = check_ws(ws, ws_bytes, index_ws_bytes(dims, cache, n_q)))) return st;
+    return run_index(dims, cache, idx_q, head_w, q_pos, n_q, pool_in, topk_out, pool_out, topk_scores, ws,
+                     static_cast<hipStream_t>(stream));
+  } catch (...) {
+    return fail(CSA2_ERR_HIP, "internal exception");
+  }
+}
+
+static int check_attn(const csa2_dims* dims, const void* q, const int32_t* q_pos, int32_t n_q, const int32_t* topk,
+                      const void* swa_kv, const int32_t* swa_first_pos, int32_t n_swa, void* out, const float* lse) {
+  int st;
+  if (n_q <= 0 || n_q > 65535) return fail(CSA2_ERR_INVALID_ARG, "n_q=%d out of range", n_q);
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(q_pos, "q_pos")) || (st = check_ptr(topk, "topk")) ||
+      (st = check_ptr(out, "out")))
+    return st;
+  if (n_swa < 0) return fail(CSA2_ERR_INVALID_ARG, "n_swa=%d is negative", n_swa);
+  if (n_swa > 0 && ((st = check_ptr(swa_kv, "swa_kv")) || (st = check_ptr(swa_first_pos, "swa_first_pos")))) return st;
+  if (lse && !aligned16(lse)) return fail(CSA2_ERR_INVALID_ARG, "lse is not 16-byte aligned");
+  return CSA2_OK;
+}
+
+int csa2_sparse_attn(const csa2_dims* dims, const csa2_kv_cache* cache, const void* q, const int32_t* q_pos,
+                     int32_t n_q, const int32_t* topk, const void* swa_kv, const int32_t* swa_first_pos,
+                     int32_t n_swa, void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  try {
+    int st;
+    if ((st = check_dims(dims)) || (st = check_cache(dims, cache, false))) return st;
+    if ((st = check_attn(dims, q, q_pos, n_q, topk, swa_kv, swa_first_pos, n_swa, out, lse))) return st;
+    if ((st = check_ws(ws, ws_bytes, csa2::attn_workspace_bytes(*dims, *cache, n_q)))) return st;
+    clear_stale_error();
+    hipError_t e = csa2::launch_attn(*dims, *cache, q, q_pos, n_q, topk, n_swa ? swa_kv : nullptr,
+                                     n_swa ? swa_first_pos : nullptr, n_swa, out, lse, ws, ws_bytes,
+                                     static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? CSA2_OK : fail_hip(e, "attention launch");
+  } catch (...) {
+    return fail(CSA2_ERR_HIP, "internal exception");
+  }
+}
+
+int csa2_layer_group(const csa2_dims* dims, const csa2_kv_cache* cache, int32_t n_layers, const csa2_layer* layers,
+                     const int32_t* q_pos, int32_t n_q, const csa2_compress_args* compress, void* ws, size_t ws_bytes,
+                     void* stream) {
+  g_last_error.clear();
+  try {
+    int st;
+    if ((st = check_dims(dims))) return st;
+    if (n_layers <= 0 || n_layers > 64) return fail(CSA2_ERR_INVALID_ARG, "n_layers=%d: need 1..64", n_layers);
+    if (!layers) return fail(CSA2_ERR_INVALID_ARG, "layers is NULL");
+    bool need_idx = compress != nullptr;
+    for (int i = 0; i < n_layers; ++i) need_idx |= layers[i].mode != CSA2_REUSE;
+    if ((st = check_cache(dims, cache, need_idx))) return st;
+    if ((st = check_ptr(q_pos, "q_pos"))) return st;
+    if (compress) {
+      if (compress->reserved0 != 0) return fail(CSA2_ERR_INVALID_ARG, "compress reserved field must be 0");
+      if ((st = check_compress(dims, cache, compress->latent, compress->first_pos, compress->n_pos,
+                               compress->pair_logits, compress->w_ik)))
+        return st;
+    }
+    for (int i = 0; i < n_layers; ++i) {
+      const csa2_layer& L = layers[i];
+      if (L.mode == CSA2_FULL) {
+        if (L.source != -1) return fail(CSA2_ERR_MODE_ORDER, "layer %d: a Full layer has no source", i);
+        if (L.make_pool && !L.pool) return fail(CSA2_ERR_INVALID_ARG, "layer %d: make_pool needs a pool buffer", i);
+      } else if (L.mode == CSA2_REINDEX) {
+        if (L.source != -1) {
+          if (L.source < 0 || L.source >= i) return fail(CSA2_ERR_MODE_ORDER, "layer %d: Reindex source %d is not an earlier layer", i, L.source);
+          const csa2_layer& S = layers[L.source];
+          if (S.mode != CSA2_FULL || !S.make_pool)
+            return fail(CSA2_ERR_MODE_ORDER, "layer %d: Reindex source %d is not a Full layer with a pool", i, L.source);
+        }
+        if (L.make_pool) return fail(CSA2_ERR_INVALID_ARG, "layer %d: only Full layers build a pool", i);
+      } else if (L.mode == CSA2_REUSE) {
+        if (L.source < 0 || L.source >= i) return fail(CSA2_ERR_MODE_ORDER, "layer %d: Reuse source %d is not an earlier layer", i, L.source);
+        if (layers[L.source].mode == CSA2_REUSE)
+          return fail(CSA2_ERR_MODE_ORDER, "layer %d: Reuse source %d must be a Full or Reindex layer", i, L.source);
+        if (L.make_pool) return fail(CSA2_ERR_INVALID_ARG, "layer %d: only Full layers build a pool", i);
+      } else {
+        return fail(CSA2_ERR_UNSUPPORTED, "layer %d: mode %d unknown", i, L.mode);
+      }
+      if (L.mode != CSA2_REUSE) {
+        if ((st = check_ptr(L.idx_q, "layer idx_q")) || (st = check_ptr(L.head_w, "layer head_w")) ||
+            (st = check_ptr(L.topk, "layer topk")))
+          return st;
+      } else if (L.topk && !aligned16(L.topk)) {
+        return fail(CSA2_ERR_INVALID_ARG, "layer %d: topk is not 16-byte aligned", i);
+      }
+      if ((st = check_attn(dims, L.q, q_pos, n_q, L.mode == CSA2_REUSE ? layers[L.source].topk : L.topk, L.swa_kv,
+                           L.swa_first_pos, L.n_swa, L.out, L.lse)))
+        return st;
+    }
+    const size_t idx_bytes = round_up(index_ws_bytes(dims, cache, n_q), kAlign);
+    const size_t attn_bytes = csa2::attn_workspace_bytes(*dims, *cache, n_q);
+    if ((st = check_ws(ws, ws_bytes, idx_bytes + attn_bytes))) return st;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (compress &&
+        (st = run_compress(dims, cache, compress->latent, compress->first_pos, compress->n_pos, compress->pair_logits,
+                           compress->w_ik, s)))
+      return st;
+    void* attn_ws = static_cast<char*>(ws) + idx_bytes;
+    for (int i = 0; i < n_layers; ++i) {
+      const csa2_layer& L = layers[i];
+      const int32_t* use_topk = L.topk;
+      if (L.mode == CSA2_FULL) {
+        if ((st = run_index(dims, cache, L.idx_q, L.head_w, q_pos, n_q, nullptr, L.topk, L.make_pool ? L.pool : nullptr,
+                            nullptr, ws, s)))
+          return st;
+      } else if (L.mode == CSA2_REINDEX) {
+        const int32_t* pool_in = L.source >= 0 ? layers[L.source].pool : nullptr;
+        if ((st = run_index(dims, cache, L.idx_q, L.head_w, q_pos, n_q, pool_in, L.topk, nullptr, nullptr, ws, s)))
+          return st;
+      } else {
+        use_topk = layers[L.source].topk;
+        if (L.topk) {
+          hipError_t e = hipMemcpyAsync(L.topk, use_topk, sizeof(int32_t) * size_t(cache->batch) * n_q * dims->topk,
+                                        hipMemcpyDeviceToDevice, s);
+          if (e != hipSuccess) return fail_hip(e, "reuse top-k copy");
+        }
+      }
+      clear_stale_error();
+      hipError_t e = csa2::launch_attn(*dims, *cache, L.q, q_pos, n_q, use_topk, L.n_swa ? L.swa_kv : nullptr,
+                                       L.n_swa ? L.swa_first_pos : nullptr, L.n_swa, L.out, L.lse, attn_ws, attn_bytes, s);
+      if (e != hipSuccess) return fail_hip(e, "attention launch");
+    }
+    return CSA2_OK;
+  } catch (...) {
+    return fail(CSA2_ERR_HIP, "internal exception");
+  }
+}
+
+}  // extern "C"

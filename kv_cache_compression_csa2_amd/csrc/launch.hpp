@@ -1,0 +1,39 @@
+// Host-side launchers of the CSA2 kernels (internal; the public ABI is csa2.h).
+// Every launcher assumes the arguments were validated by abi.cpp and returns
+// the hipError_t of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "csa2.h"
+
+namespace csa2 {
+
+// Scratch layout of one index_topk call (all float32, per (batch, query)).
+struct ScanScratch {
+  float* scores;  // [batch*n_q][dom_cap]
+  float* bmax;    // [batch*n_q][dom_cap/8]
+  float* sbmax;   // [batch*n_q][dom_cap/64]
+  int64_t dom_cap;  // multiple of 64
+};
+
+hipError_t launch_compress(const csa2_dims& dims, const csa2_kv_cache& cache, const void* latent,
+                           const int32_t* first_pos, int32_t n_pos, const float* pair_logits, const void* w_ik,
+                           hipStream_t stream);
+
+hipError_t launch_scan(const csa2_dims& dims, const csa2_kv_cache& cache, const void* idx_q, const float* head_w,
+                       const int32_t* q_pos, int32_t n_q, const int32_t* pool_in, const ScanScratch& ss,
+                       hipStream_t stream);
+
+hipError_t launch_select(const csa2_dims& dims, const csa2_kv_cache& cache, const int32_t* q_pos, int32_t n_q,
+                         const int32_t* pool_in, const ScanScratch& ss, int32_t* topk_out, int32_t* pool_out,
+                         float* topk_scores, hipStream_t stream);
+
+hipError_t launch_attn(const csa2_dims& dims, const csa2_kv_cache& cache, const void* q, const int32_t* q_pos,
+                       int32_t n_q, const int32_t* topk, const void* swa_kv, const int32_t* swa_first_pos,
+                       int32_t n_swa, void* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+
+size_t attn_workspace_bytes(const csa2_dims& dims, const csa2_kv_cache& cache, int32_t n_q);
+
+}  // namespace csa2
