@@ -76,11 +76,182 @@ __global__ __launch_bounds__(kThreads) void scan_generic_kernel(
   }
 }
 
+
+// ------------------------------------------------------------------ MFMA ---
+//
+// Production shape: 32 indexer heads x 128, bf16 queries, bf16 or FP4 (one
+// E4M3 scale per 32 channels) indexer K.  The per-tile contraction
+// S[head][entry] = Q[32 x 128] . K^T[128 x 32] runs as eight
+// v_mfma_f32_32x32x16_bf16.  Operands come straight from memory in MFMA
+// layout: lane l supplies row (l % 32) with eight consecutive k of its half
+// (l / 32); the order in which k is visited is free, so it is chosen to make
+// each lane's K bytes contiguous (bf16: one 128-byte run per lane) or to keep
+// every step inside one FP4 scale group (FP4: the group scale is applied to
+// the step-group's partial sum after the MFMA, because the hardware's scaled
+// FP4 convert honours only the exponent of its scale).  Accumulator lane l
+// register r holds head 8*(r/4) + 4*(l/32) + r%4 of entry l % 32; the head
+// sum w_h * ReLU(.) runs in registers, then one cross-half shuffle completes
+// the entry score.
+//
+// A workgroup (4 waves) covers 16 super-blocks of 64 domain slots; wave w
+// takes super-blocks w, w+4, w+8, w+12, two 32-entry tiles each.
+
+typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
+typedef __bf16 bf16x2_t __attribute__((__vector_size__(4)));
+typedef float f32x16_t __attribute__((__vector_size__(64)));
+
+constexpr int kSbPerWave = 4;
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// Eight E2M1 codes (one dword, low nibble first) -> eight exact bf16 values.
+__device__ __forceinline__ bf16x8_t fp4x8_to_bf16(uint32_t w) {
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3);
+  uint4 v;
+  v.x = __builtin_bit_cast(uint32_t, a);
+  v.y = __builtin_bit_cast(uint32_t, b);
+  v.z = __builtin_bit_cast(uint32_t, c);
+  v.w = __builtin_bit_cast(uint32_t, d);
+  return as_bf16x8(v);
+}
+
+template <bool FP4>
+__global__ __launch_bounds__(256, 2) void scan_mfma_kernel(
+    int ratio, int64_t capacity, const uint16_t* __restrict__ idx_q, const float* __restrict__ head_w,
+    const int32_t* __restrict__ q_pos, int n_q, const int32_t* __restrict__ pool_in, int cand_blocks,
+    const uint8_t* __restrict__ idx_k, const uint8_t* __restrict__ idx_scale, const int32_t* __restrict__ n_entries,
+    float* __restrict__ scores, float* __restrict__ bmax, float* __restrict__ sbmax, int64_t dom_cap) {
+  constexpr int kBatch = FP4 ? 4 : 1;  // super-blocks whose loads are issued together
+  constexpr int kTiles = 2 * kBatch;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 31, h = lane >> 5;
+  const int qi = blockIdx.y, b = blockIdx.z;
+  const int64_t row = int64_t(b) * n_q + qi;
+  const int64_t nsb = dom_cap / 64;
+  const int64_t n_vis = visible_count(clamp_entries(n_entries, b, capacity), q_pos[row], ratio);
+
+  // A operand (indexer query) and the lane's 16 head weights, held for the whole scan
+  bf16x8_t qop[8];
+  const uint16_t* qrow = idx_q + (row * 32 + n) * 128;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int k0 = FP4 ? 32 * (s >> 1) + 16 * h + 8 * (s & 1) : 64 * h + 8 * s;
+    qop[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + k0));
+  }
+  float wreg[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) wreg[r] = head_w[row * 32 + 8 * (r >> 2) + 4 * h + (r & 3)];
+
+  const int64_t sb0 = int64_t(blockIdx.x) * (4 * kSbPerWave) + wave;
+  for (int it = 0; it < kSbPerWave; it += kBatch) {
+    const int64_t sb_first = sb0 + 4 * it;
+    if (sb_first >= nsb) break;
+    const bool any_visible = pool_in || sb_first * 64 < n_vis;
+
+    // ---- issue the loads of kTiles tiles ----
+    int64_t slot[kTiles];
+    bool valid[kTiles];
+    uint4 kb[FP4 ? 1 : kTiles][8];
+    uint2 kf[FP4 ? kTiles : 1][4];
+    uint32_t ks[FP4 ? kTiles : 1];
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+      const int64_t sb = sb_first + 4 * (t >> 1);
+      slot[t] = sb * 64 + 32 * (t & 1) + n;
+      int64_t j = -1;
+      if (sb < nsb && any_visible) {
+        if (pool_in) {
+          const int64_t blk = slot[t] / 8 < cand_blocks ? pool_in[row * cand_blocks + slot[t] / 8] : -1;
+          if (blk >= 0) j = blk * 8 + (slot[t] & 7);
+        } else {
+          j = slot[t];
+        }
+      }
+      valid[t] = j >= 0 && j < n_vis;
+      const int64_t crow = int64_t(b) * capacity + (valid[t] ? j : 0);
+      if (any_visible) {
+        if (FP4) {
+          const uint8_t* p = idx_k + crow * 64 + 8 * h;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) kf[t][g] = *reinterpret_cast<const uint2*>(p + 16 * g);
+          ks[t] = *reinterpret_cast<const uint32_t*>(idx_scale + crow * 4);
+        } else {
+          const uint4* p = reinterpret_cast<const uint4*>(idx_k + (crow * 128 + 64 * h) * 2);
+#pragma unroll
+          for (int s = 0; s < 8; ++s) kb[t][s] = p[s];
+        }
+      }
+    }
+
+    // ---- contract, reduce over heads, write scores and maxima ----
+    float tmax[kTiles];
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+      float part = 0.0f;
+      if (any_visible) {
+        if (FP4) {
+          f32x16_t acc[4];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            acc[g] = f32x16_t{};
+            acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qop[2 * g], fp4x8_to_bf16(kf[t][g].x), acc[g], 0, 0, 0);
+            acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qop[2 * g + 1], fp4x8_to_bf16(kf[t][g].y), acc[g], 0, 0, 0);
+          }
+          const float s0 = e4m3_to_f32(ks[t] & 0xFF), s1 = e4m3_to_f32((ks[t] >> 8) & 0xFF);
+          const float s2 = e4m3_to_f32((ks[t] >> 16) & 0xFF), s3 = e4m3_to_f32(ks[t] >> 24);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float dot = s0 * acc[0][r] + s1 * acc[1][r] + s2 * acc[2][r] + s3 * acc[3][r];
+            part += wreg[r] * fmaxf(dot, 0.0f);
+          }
+        } else {
+          f32x16_t acc = f32x16_t{};
+#pragma unroll
+          for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qop[s], as_bf16x8(kb[t][s]), acc, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) part += wreg[r] * fmaxf(acc[r], 0.0f);
+        }
+      }
+      float sc = part + __shfl_xor(part, 32, kWave);
+      if (!valid[t]) sc = -INFINITY;
+      const int64_t sb = sb_first + 4 * (t >> 1);
+      if (sb < nsb && h == 0) scores[row * dom_cap + slot[t]] = sc;
+      float m = fmaxf(sc, __shfl_xor(sc, 1, kWave));
+      m = fmaxf(m, __shfl_xor(m, 2, kWave));
+      m = fmaxf(m, __shfl_xor(m, 4, kWave));
+      if (sb < nsb && h == 0 && (n & 7) == 0) bmax[row * (dom_cap / 8) + slot[t] / 8] = m;
+      m = fmaxf(m, __shfl_xor(m, 8, kWave));
+      m = fmaxf(m, __shfl_xor(m, 16, kWave));
+      tmax[t] = m;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t sb = sb_first + 4 * u;
+      if (sb < nsb && lane == 0) sbmax[row * nsb + sb] = fmaxf(tmax[2 * u], tmax[2 * u + 1]);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_scan(const csa2_dims& dims, const csa2_kv_cache& cache, const void* idx_q, const float* head_w,
                        const int32_t* q_pos, int32_t n_q, const int32_t* pool_in, const ScanScratch& ss,
                        hipStream_t stream) {
+  const bool mfma_shape = dims.n_idx_heads == 32 && dims.d_idx == 128 && dims.act_dtype == CSA2_BF16 &&
+                          (cache.kv_dtype == CSA2_BF16 || (cache.kv_dtype == CSA2_FP4 && cache.idx_group == 32));
+  if (mfma_shape) {
+    const int64_t nsb = ss.dom_cap / 64;
+    const dim3 grid(unsigned((nsb + 4 * kSbPerWave - 1) / (4 * kSbPerWave)), n_q, cache.batch);
+    auto kern = cache.kv_dtype == CSA2_FP4 ? scan_mfma_kernel<true> : scan_mfma_kernel<false>;
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, cache.ratio, cache.capacity,
+                       static_cast<const uint16_t*>(idx_q), head_w, q_pos, n_q, pool_in, dims.cand_blocks,
+                       static_cast<const uint8_t*>(cache.idx_k), cache.idx_scale, cache.n_entries, ss.scores, ss.bmax,
+                       ss.sbmax, ss.dom_cap);
+    return hipGetLastError();
+  }
   const dim3 grid(unsigned(ss.dom_cap / kThreads), n_q, cache.batch);
   const size_t lds = sizeof(float) * size_t(dims.n_idx_heads * dims.d_idx + dims.n_idx_heads + kThreads);
   hipLaunchKernelGGL(scan_generic_kernel, grid, dim3(kThreads), lds, stream, dims.n_idx_heads, dims.d_idx,
