@@ -80,7 +80,7 @@ typedef enum csa2_entry_point {
 /* Shape of one CSA2 layer ([ZB] section 1.2 hyper-parameters). */
 typedef struct csa2_dims {
   int32_t d;           /* latent width = query head width (512); multiple of 32 */
-  int32_t d_rope;      /* trailing rotary channels of the latent (64); even, <= d */
+  int32_t d_rope;      /* trailing rotary channels of the latent (64); even, <= min(d, 128) */
   int32_t n_heads;     /* main query heads (64) */
   int32_t n_idx_heads; /* indexer heads (32) */
   int32_t d_idx;       /* indexer head width = indexer-K width (128); multiple of 32 */

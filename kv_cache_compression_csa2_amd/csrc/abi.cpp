@@ -42,6 +42,7 @@ int check_dims(const csa2_dims* d) {
   if (!d) return fail(CSA2_ERR_INVALID_ARG, "dims is NULL");
   if (d->d <= 0 || d->d % 32 || d->d > 1024) return fail(CSA2_ERR_UNSUPPORTED, "d=%d: need a multiple of 32 in [32, 1024]", d->d);
   if (d->d_rope < 0 || d->d_rope % 2 || d->d_rope > d->d) return fail(CSA2_ERR_INVALID_ARG, "d_rope=%d: need even, 0..d", d->d_rope);
+  if (d->d_rope > 128) return fail(CSA2_ERR_UNSUPPORTED, "d_rope=%d: at most 128 rotary channels", d->d_rope);
   if (d->n_heads <= 0 || d->n_heads > 1024) return fail(CSA2_ERR_INVALID_ARG, "n_heads=%d out of range", d->n_heads);
   if (d->n_idx_heads <= 0 || d->d_idx <= 0 || d->d_idx % 32 || d->d_idx > 512)
     return fail(CSA2_ERR_UNSUPPORTED, "indexer heads %d x %d: need width a multiple of 32 up to 512", d->n_idx_heads, d->d_idx);

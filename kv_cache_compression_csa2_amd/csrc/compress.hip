@@ -52,14 +52,18 @@ __device__ void store_row(const double* v, int n, int dtype, int group, void* ba
   }
 }
 
+// ACT_BF16 is a template parameter: a runtime dtype branch inside the
+// unrolled W_ik loop would make the compiler wait for every load in turn.
+template <bool ACT_BF16>
 __global__ __launch_bounds__(kThreads) void compress_kernel(
-    int d, int d_rope, int d_idx, int act_bf16, int kv_dtype, int main_group, int idx_group, int ratio,
-    int64_t capacity, double theta, const void* __restrict__ latent, const int32_t* __restrict__ first_pos,
+    int d, int d_rope, int d_idx, int kv_dtype, int main_group, int idx_group, int ratio,
+    int64_t capacity, RopeTable rope, const void* __restrict__ latent, const int32_t* __restrict__ first_pos,
     int n_pos, const float* __restrict__ pair_logits, const void* __restrict__ w_ik, void* main,
     uint8_t* main_scale, void* idx_k, uint8_t* idx_scale) {
   extern __shared__ double sh[];
   double* e = sh;       // [d]  merged, then rotated entry
   double* kap = sh + d;  // [d_idx] projection
+  constexpr int act_bf16 = ACT_BF16 ? 1 : 0;
   const int m = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int64_t fp = first_pos[b];
   if (fp < 0 || fp % ratio) return;
@@ -91,7 +95,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
   const double p = double(int64_t(ratio) * j + ratio - 1);
   const int c0 = d - d_rope;
   for (int mm = tid; mm < d_rope / 2; mm += kThreads) {
-    const double freq = pow(theta, -2.0 * mm / d_rope);
+    const double freq = rope.inv_freq[mm];
     double sn, cs;
     sincos(p * freq, &sn, &cs);
     const double x = e[c0 + 2 * mm], y = e[c0 + 2 * mm + 1];
@@ -103,11 +107,58 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
   // 3. main KV row
   store_row(e, d, kv_dtype, main_group, main, main_scale, row);
 
-  // 4. indexer K = e_hat . W_ik, from the unrounded rotated entry
-  for (int o = tid; o < d_idx; o += kThreads) {
-    double acc = 0.0;
-    for (int c = 0; c < d; ++c) acc += e[c] * double(act_load(w_ik, int64_t(c) * d_idx + o, act_bf16));
-    kap[o] = acc;
+  // 4. indexer K = e_hat . W_ik, from the unrounded rotated entry.  Thread
+  // (part, pair) sums output channels 2*pair, 2*pair+1 over a slice of the
+  // input channels; W_ik rows are read as contiguous pairs, 64 loads in
+  // flight before the FMAs (this kernel is latency-bound, not
+  // bandwidth-bound); the float64 partials are added through LDS.
+  {
+    const int pairs = d_idx / 2;
+    const int parts = kThreads / pairs > 0 ? kThreads / pairs : 1;
+    const int pair = tid % pairs, part = tid / pairs;
+    const int span = (d + parts - 1) / parts;
+    double* red = kap + d_idx;  // [parts][d_idx]
+    if (part < parts) {
+      double a0 = 0.0, a1 = 0.0;
+      const int c_lo = part * span, c_hi = min(d, c_lo + span);
+      for (int p0 = pair; p0 < pairs; p0 += kThreads) {
+        a0 = a1 = 0.0;
+        int c = c_lo;
+        for (; c + 64 <= c_hi; c += 64) {
+          float w0[64], w1[64];
+#pragma unroll
+          for (int u = 0; u < 64; ++u) {
+            const int64_t off = int64_t(c + u) * d_idx + 2 * p0;
+            if constexpr (ACT_BF16) {
+              const uint32_t two = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(w_ik) + off);
+              w0[u] = bf16_to_f32(uint16_t(two & 0xFFFFu));
+              w1[u] = bf16_to_f32(uint16_t(two >> 16));
+            } else {
+              const float2 two = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(w_ik) + off);
+              w0[u] = two.x;
+              w1[u] = two.y;
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < 64; ++u) {
+            a0 += e[c + u] * double(w0[u]);
+            a1 += e[c + u] * double(w1[u]);
+          }
+        }
+        for (; c < c_hi; ++c) {
+          a0 += e[c] * double(act_load(w_ik, int64_t(c) * d_idx + 2 * p0, act_bf16));
+          a1 += e[c] * double(act_load(w_ik, int64_t(c) * d_idx + 2 * p0 + 1, act_bf16));
+        }
+        red[part * d_idx + 2 * p0] = a0;
+        red[part * d_idx + 2 * p0 + 1] = a1;
+      }
+    }
+    __syncthreads();
+    for (int o = tid; o < d_idx; o += kThreads) {
+      double acc = 0.0;
+      for (int x = 0; x < parts; ++x) acc += red[x * d_idx + o];
+      kap[o] = acc;
+    }
   }
   __syncthreads();
   store_row(kap, d_idx, kv_dtype, idx_group, idx_k, idx_scale, row);
@@ -119,10 +170,11 @@ hipError_t launch_compress(const csa2_dims& dims, const csa2_kv_cache& cache, co
                            const int32_t* first_pos, int32_t n_pos, const float* pair_logits, const void* w_ik,
                            hipStream_t stream) {
   const dim3 grid(n_pos / cache.ratio, cache.batch);
-  const size_t lds = sizeof(double) * size_t(dims.d + dims.d_idx);
-  hipLaunchKernelGGL(compress_kernel, grid, dim3(kThreads), lds, stream, dims.d, dims.d_rope, dims.d_idx,
-                     int(dims.act_dtype == CSA2_BF16), cache.kv_dtype, cache.main_group, cache.idx_group, cache.ratio,
-                     cache.capacity, dims.rope_theta, latent, first_pos, n_pos, pair_logits, w_ik, cache.main,
+  const int parts = kThreads / (dims.d_idx / 2) > 0 ? kThreads / (dims.d_idx / 2) : 1;
+  const size_t lds = sizeof(double) * size_t(dims.d + dims.d_idx + parts * dims.d_idx);
+  auto kern = dims.act_dtype == CSA2_BF16 ? compress_kernel<true> : compress_kernel<false>;
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, stream, dims.d, dims.d_rope, dims.d_idx, cache.kv_dtype, cache.main_group, cache.idx_group, cache.ratio,
+                     cache.capacity, make_rope_table(dims), latent, first_pos, n_pos, pair_logits, w_ik, cache.main,
                      cache.main_scale, cache.idx_k, cache.idx_scale);
   return hipGetLastError();
 }

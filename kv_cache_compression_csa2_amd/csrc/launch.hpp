@@ -6,9 +6,24 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cmath>
+
 #include "csa2.h"
 
 namespace csa2 {
+
+// Inverse RoPE frequencies theta^(-2m/d_rope) for pair m, computed once per
+// launch on the host (libm pow, float64) and passed by value to the kernels,
+// so no kernel evaluates a float64 pow per element.
+struct RopeTable {
+  double inv_freq[64];
+};
+
+inline RopeTable make_rope_table(const csa2_dims& d) {
+  RopeTable t{};
+  for (int m = 0; m < d.d_rope / 2 && m < 64; ++m) t.inv_freq[m] = std::pow(d.rope_theta, -2.0 * m / d.d_rope);
+  return t;
+}
 
 // Scratch layout of one index_topk call (all float32, per (batch, query)).
 struct ScanScratch {

@@ -21,8 +21,10 @@
 //
 // Each level is a radix select over at most 16384 keys held in LDS: three
 // histogram passes (11, 11, 10 bits of the order-preserving key) find the
-// threshold key and how many ties to keep; ties go to the lowest positions;
-// an order-preserving compaction (wave ballots + a scan over waves) emits the
+// threshold key and how many ties to keep; after the first pass only the keys
+// of the threshold bin are revisited (gathered into a short list when they
+// fit); one wave scans each histogram; ties go to the lowest positions; an
+// order-preserving compaction (wave ballots + a scan over waves) emits the
 // chosen positions ascending.  One 1024-thread workgroup per (sequence, query).
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -34,65 +36,97 @@ constexpr int kNT = 1024;
 constexpr int kNW = kNT / kWave;
 constexpr int kMaxCand = 16384;
 constexpr int kMaxList = 2048;
+// Histogram bin b lives at word b + b/32: the single wave that scans the bins
+// reads 32 consecutive bins per lane, and the pad puts the lanes on distinct
+// LDS banks.
+constexpr int kHistWords = 2048 + 2048 / 32;
+__device__ __forceinline__ int hbin(int b) { return b + (b >> 5); }
 
 struct SelLds {
   uint32_t* keys;  // [kMaxCand]
   uint32_t* la;    // [kMaxList]
   uint32_t* lb;    // [kMaxList]
-  uint32_t* hist;  // [2048]
+  uint32_t* cand;  // [kMaxList] keys sharing the threshold prefix (unordered)
+  uint32_t* hist;  // [kHistWords] padded bins (see hbin), all zero between passes
   uint32_t* wsum;  // [2 * kNW]
-  uint32_t* scan;  // [kNW + 1]
   uint32_t* misc;  // [8]
 };
 
 __device__ __forceinline__ uint64_t lanemask_lt() { return (uint64_t(1) << (threadIdx.x & 63)) - 1; }
 
+// Wave 0 only: find the bin holding the need-th largest key among nb bins of
+// hist (digits compared from the top), write {bin, need left inside it,
+// total count, bin count} to misc[0..3], and clear the bins.
+__device__ __forceinline__ void find_digit(const SelLds& L, int nb, uint32_t need) {
+  const int lane = threadIdx.x & 63;
+  const int per = nb / kWave;
+  uint32_t s = 0;
+  for (int x = 0; x < per; ++x) s += L.hist[hbin(lane * per + x)];
+  const uint32_t incl = wave_inclusive_scan(s);
+  const uint32_t total = __shfl(incl, kWave - 1, kWave);
+  uint32_t above = total - incl;  // keys in the bins of higher lanes
+  if (above < need && need <= above + s) {
+    for (int x = per - 1; x >= 0; --x) {
+      const int bin = lane * per + x;
+      const uint32_t h = L.hist[hbin(bin)];
+      if (above < need && need <= above + h) {
+        L.misc[0] = uint32_t(bin);
+        L.misc[1] = need - above;
+        L.misc[3] = h;
+      }
+      above += h;
+    }
+  }
+  if (lane == 0) {
+    L.misc[2] = total;
+    L.misc[4] = 0;  // candidate-list fill counter
+  }
+  for (int x = 0; x < per; ++x) L.hist[hbin(lane * per + x)] = 0;
+}
+
 // Select the best min(m, #valid) of keys[0..n) (valid: key > kKeyNegInf),
 // ties to the lower position; write the chosen positions ascending to out[].
-// Returns the number chosen.  All threads of the block must call it.
+// Returns the number chosen.  All threads of the block must call it; hist
+// must be zero on entry and is zero on exit.
 __device__ int select_top(const SelLds& L, int n, int m, uint32_t* out) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int seg = (((n + kNW - 1) / kNW) + 63) & ~63;
   const int lo = w * seg, hi = min(n, lo + seg);
 
-  // number of valid keys
-  uint32_t cnt = 0;
-  for (int p = lo + lane; p < hi; p += kWave) cnt += L.keys[p] > kKeyNegInf;
-  uint32_t total;
-  block_exclusive_scan<kNT>(cnt, L.scan, total);
-
+  // pass 1 over every key: top 11 bits
+  for (int p = lo + lane; p < hi; p += kWave) {
+    const uint32_t k = L.keys[p];
+    if (k > kKeyNegInf) atomicAdd(&L.hist[hbin(int(k >> 21))], 1u);
+  }
+  __syncthreads();
+  if (w == 0) find_digit(L, 2048, uint32_t(m));
+  __syncthreads();
+  const uint32_t total = L.misc[2];
   uint32_t T = kKeyNegInf, need_eq = 0;
   if (total > uint32_t(m)) {
-    uint32_t prefix = 0, mask = 0, need = uint32_t(m);
-    const int shifts[3] = {21, 10, 0};
-    const int bits[3] = {11, 11, 10};
-    for (int pass = 0; pass < 3; ++pass) {
-      const int sh = shifts[pass], nb = 1 << bits[pass];
-      const uint32_t dmask = uint32_t(nb - 1);
-      for (int x = tid; x < nb; x += kNT) L.hist[x] = 0;
-      __syncthreads();
+    uint32_t prefix = L.misc[0] << 21, mask = 0xFFE00000u, need = L.misc[1];
+    const bool use_list = L.misc[3] <= uint32_t(kMaxList);
+    if (use_list) {  // gather the keys of the threshold bin once; later passes read only them
       for (int p = lo + lane; p < hi; p += kWave) {
         const uint32_t k = L.keys[p];
-        if (k > kKeyNegInf && (k & mask) == prefix) atomicAdd(&L.hist[(k >> sh) & dmask], 1u);
+        if (k > kKeyNegInf && (k & mask) == prefix) L.cand[atomicAdd(&L.misc[4], 1u)] = k;
       }
       __syncthreads();
-      // thread t owns the reversed chunk r = NT-1-t of bins; an exclusive scan
-      // in thread order then counts the keys in every higher bin
-      const int per = nb / kNT;
-      const int r = kNT - 1 - tid;
-      uint32_t local = 0;
-      for (int x = 0; x < per; ++x) local += L.hist[r * per + x];
-      uint32_t tot2;
-      uint32_t above = block_exclusive_scan<kNT>(local, L.scan, tot2);
-      for (int x = per - 1; x >= 0; --x) {
-        const int bin = r * per + x;
-        const uint32_t h = L.hist[bin];
-        if (above < need && need <= above + h) {
-          L.misc[0] = uint32_t(bin);
-          L.misc[1] = need - above;
-        }
-        above += h;
+    }
+    const int nc = use_list ? int(L.misc[4]) : n;
+    const int cseg = (((nc + kNW - 1) / kNW) + 63) & ~63;
+    const int clo = w * cseg, chi = min(nc, clo + cseg);
+    const int shifts[2] = {10, 0};
+    const int bits[2] = {11, 10};
+    for (int pass = 0; pass < 2; ++pass) {
+      const int sh = shifts[pass];
+      const uint32_t dmask = (1u << bits[pass]) - 1u;
+      for (int p = clo + lane; p < chi; p += kWave) {
+        const uint32_t k = use_list ? L.cand[p] : L.keys[p];
+        if (k > kKeyNegInf && (k & mask) == prefix) atomicAdd(&L.hist[hbin(int((k >> sh) & dmask))], 1u);
       }
+      __syncthreads();
+      if (w == 0) find_digit(L, 1 << bits[pass], need);
       __syncthreads();
       prefix |= L.misc[0] << sh;
       mask |= dmask << sh;
@@ -164,10 +198,11 @@ __global__ __launch_bounds__(kNT) void select_kernel(int topk, int cand_blocks, 
   L.keys = lds;
   L.la = L.keys + kMaxCand;
   L.lb = L.la + kMaxList;
-  L.hist = L.lb + kMaxList;
-  L.wsum = L.hist + 2048;
-  L.scan = L.wsum + 2 * kNW;
-  L.misc = L.scan + kNW + 1;
+  L.cand = L.lb + kMaxList;
+  L.hist = L.cand + kMaxList;
+  L.wsum = L.hist + kHistWords;
+  L.misc = L.wsum + 2 * kNW;
+  for (int x = threadIdx.x; x < kHistWords; x += kNT) L.hist[x] = 0;
 
   const int qi = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int64_t row = int64_t(b) * n_q + qi;
@@ -225,8 +260,7 @@ __global__ __launch_bounds__(kNT) void select_kernel(int topk, int cand_blocks, 
   }
 }
 
-constexpr size_t kSelectLds =
-    sizeof(uint32_t) * (kMaxCand + 2 * kMaxList + 2048 + 2 * kNW + kNW + 1 + 8);
+constexpr size_t kSelectLds = sizeof(uint32_t) * (kMaxCand + 3 * kMaxList + kHistWords + 2 * kNW + 8);
 
 }  // namespace
 

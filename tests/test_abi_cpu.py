@@ -146,6 +146,14 @@ def test_layer_group_mode_order(layers, status):
                                 1 << 40, None) == status
 
 
+@pytest.mark.parametrize("heads,d", [(8, 64), (64, 512), (32, 512), (1, 32)])
+def test_workspace_size_any_head_count(heads, d):
+    """Sizing never divides by a head-group count (8 heads, 64-d is the tiny workload)."""
+    n = B.csa2_workspace_size(dims(n_heads=heads, d=d, d_rope=16), cache(), B.EP_SPARSE_ATTN, 16)
+    assert n >= 0
+    assert B.csa2_workspace_size(dims(n_heads=heads, d=d, d_rope=16), cache(), B.EP_LAYER_GROUP, 16) > 0
+
+
 def test_workspace_size():
     d, c = dims(), cache()
     n = B.csa2_workspace_size(d, c, B.EP_INDEX_TOPK, 1)
