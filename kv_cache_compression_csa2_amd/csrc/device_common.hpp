@@ -9,6 +9,14 @@ namespace csa2 {
 
 constexpr int kWave = 64;
 
+// Pointer into LDS that keeps its address space through structs and calls, so
+// accesses compile to ds_* instructions instead of generic (flat) ones.
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+
+__device__ __forceinline__ void lds_inc(lds_u32* p) {
+  __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
 // ---------------------------------------------------------------- bfloat16 --
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }

@@ -18,16 +18,20 @@
 // slots) inside them -> top-k slots inside those blocks.  The pool is found
 // the same way with the forced block and its super-block given a key above
 // every score (the argument then runs over the remaining kappa-1 places).
+// A level whose candidates number at most m keeps them all and is skipped.
 //
-// Each level is a radix select over at most 16384 keys held in LDS: three
-// histogram passes (11, 11, 10 bits of the order-preserving key) find the
-// threshold key and how many ties to keep; after the first pass only the keys
-// of the threshold bin are revisited (gathered into a short list when they
-// fit); one wave scans each histogram; ties go to the lowest positions; an
-// order-preserving compaction (wave ballots + a scan over waves) emits the
-// chosen positions ascending.  One 1024-thread workgroup per (sequence, query).
+// Each level selects among at most 16384 keys (see select_top).  The step is
+// latency-bound (one workgroup per query), so the work of every level is
+// spread over 16 waves with short rolled loops, wave reductions and scans run
+// on DPP, and LDS is addressed through address-space-3 pointers so every
+// access is a ds_* instruction.
 #include "device_common.hpp"
 #include "launch.hpp"
+
+extern "C" __device__ uint32_t __ockl_wfscan_add_u32(uint32_t, bool);
+extern "C" __device__ uint32_t __ockl_wfred_add_u32(uint32_t);
+extern "C" __device__ uint32_t __ockl_wfred_min_u32(uint32_t);
+extern "C" __device__ uint32_t __ockl_wfred_max_u32(uint32_t);
 
 namespace csa2 {
 namespace {
@@ -36,146 +40,155 @@ constexpr int kNT = 1024;
 constexpr int kNW = kNT / kWave;
 constexpr int kMaxCand = 16384;
 constexpr int kMaxList = 2048;
-// Histogram bin b lives at word b + b/32: the single wave that scans the bins
-// reads 32 consecutive bins per lane, and the pad puts the lanes on distinct
-// LDS banks.
-constexpr int kHistWords = 2048 + 2048 / 32;
-__device__ __forceinline__ int hbin(int b) { return b + (b >> 5); }
+constexpr int kBins = 2048;
+constexpr int kBinsPerWave = kBins / kNW;  // 128: two per lane
 
 struct SelLds {
-  uint32_t* keys;  // [kMaxCand]
-  uint32_t* la;    // [kMaxList]
-  uint32_t* lb;    // [kMaxList]
-  uint32_t* cand;  // [kMaxList] keys sharing the threshold prefix (unordered)
-  uint32_t* hist;  // [kHistWords] padded bins (see hbin), all zero between passes
-  uint32_t* wsum;  // [2 * kNW]
-  uint32_t* misc;  // [8]
+  lds_u32* keys;  // [kMaxCand] candidate keys by position
+  lds_u32* la;    // [kMaxList]
+  lds_u32* lb;    // [kMaxList]
+  lds_u32* hist;  // [kBins], all zero between passes
+  lds_u32* wred;  // [4 * kNW] per-wave partial results
+  lds_u32* misc;  // [8]
 };
 
-__device__ __forceinline__ uint64_t lanemask_lt() { return (uint64_t(1) << (threadIdx.x & 63)) - 1; }
-
-// Wave 0 only: find the bin holding the need-th largest key among nb bins of
-// hist (digits compared from the top), write {bin, need left inside it,
-// total count, bin count} to misc[0..3], and clear the bins.
-__device__ __forceinline__ void find_digit(const SelLds& L, int nb, uint32_t need) {
+// Reduce the kNW per-wave values wred[base .. base+kNW) with lanes < kNW of
+// the calling wave; op 0 = sum, 1 = min, 2 = max.
+__device__ __forceinline__ uint32_t reduce_waves(const SelLds L, int base, int op) {
   const int lane = threadIdx.x & 63;
-  const int per = nb / kWave;
-  uint32_t s = 0;
-  for (int x = 0; x < per; ++x) s += L.hist[hbin(lane * per + x)];
-  const uint32_t incl = wave_inclusive_scan(s);
-  const uint32_t total = __shfl(incl, kWave - 1, kWave);
-  uint32_t above = total - incl;  // keys in the bins of higher lanes
-  if (above < need && need <= above + s) {
-    for (int x = per - 1; x >= 0; --x) {
-      const int bin = lane * per + x;
-      const uint32_t h = L.hist[hbin(bin)];
-      if (above < need && need <= above + h) {
-        L.misc[0] = uint32_t(bin);
-        L.misc[1] = need - above;
-        L.misc[3] = h;
-      }
-      above += h;
-    }
-  }
-  if (lane == 0) {
-    L.misc[2] = total;
-    L.misc[4] = 0;  // candidate-list fill counter
-  }
-  for (int x = 0; x < per; ++x) L.hist[hbin(lane * per + x)] = 0;
+  const uint32_t ident = op == 1 ? 0xFFFFFFFFu : 0u;
+  const uint32_t v = lane < kNW ? L.wred[base + lane] : ident;
+  return op == 0 ? __ockl_wfred_add_u32(v) : (op == 1 ? __ockl_wfred_min_u32(v) : __ockl_wfred_max_u32(v));
+}
+
+// Exclusive prefix over waves of the kNW values wred[base ..]: the sum of the
+// values of the waves before wave w.
+__device__ __forceinline__ uint32_t waves_before(const SelLds L, int base, int w) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t v = lane < kNW ? L.wred[base + lane] : 0u;
+  const uint32_t incl = __ockl_wfscan_add_u32(v, true);
+  return w == 0 ? 0u : uint32_t(__builtin_amdgcn_readlane(int(incl), w - 1));
 }
 
 // Select the best min(m, #valid) of keys[0..n) (valid: key > kKeyNegInf),
 // ties to the lower position; write the chosen positions ascending to out[].
-// Returns the number chosen.  All threads of the block must call it; hist
-// must be zero on entry and is zero on exit.
-__device__ int select_top(const SelLds& L, int n, int m, uint32_t* out) {
+// Returns the number chosen.  All threads of the block must call it; hist is
+// zero on entry and on exit.
+//
+// The threshold key T is found by narrowing a key interval [lo, hi] that
+// holds it: each pass splits the interval into at most 2048 equal bins, and
+// the interval shrinks to the bin that holds the need-th largest key.
+// Starting from the observed [min, max] of the keys spreads similar scores
+// over many bins, so the LDS histogram atomics rarely collide; three passes
+// always suffice for 32-bit keys.  Wave w owns positions [w*seg, w*seg+seg)
+// and bins [128w, 128w+128); all loops are short and rolled, since a single
+// wave retires dependent instructions slowly and this step is latency-bound.
+__device__ int select_top(const SelLds L, int n, int m, lds_u32* out) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int seg = (((n + kNW - 1) / kNW) + 63) & ~63;
-  const int lo = w * seg, hi = min(n, lo + seg);
+  const int lo_p = w * seg, hi_p = min(n, lo_p + seg);
 
-  // pass 1 over every key: top 11 bits
-  for (int p = lo + lane; p < hi; p += kWave) {
+  // count, min and max of the valid keys
+  uint32_t cnt = 0, kmn = 0xFFFFFFFFu, kmx = 0u;
+  for (int p = lo_p + lane; p < hi_p; p += kWave) {
     const uint32_t k = L.keys[p];
-    if (k > kKeyNegInf) atomicAdd(&L.hist[hbin(int(k >> 21))], 1u);
+    if (k > kKeyNegInf) {
+      ++cnt;
+      kmn = min(kmn, k);
+      kmx = max(kmx, k);
+    }
+  }
+  cnt = __ockl_wfred_add_u32(cnt);
+  kmn = __ockl_wfred_min_u32(kmn);
+  kmx = __ockl_wfred_max_u32(kmx);
+  if (lane == 0) {
+    L.wred[w] = cnt;
+    L.wred[kNW + w] = kmn;
+    L.wred[2 * kNW + w] = kmx;
   }
   __syncthreads();
-  if (w == 0) find_digit(L, 2048, uint32_t(m));
+  const uint32_t total = reduce_waves(L, 0, 0);
+  uint32_t lo = reduce_waves(L, kNW, 1), hi = reduce_waves(L, 2 * kNW, 2);
   __syncthreads();
-  const uint32_t total = L.misc[2];
-  uint32_t T = kKeyNegInf, need_eq = 0;
+
+  uint32_t T = kKeyNegInf, need = 0;
   if (total > uint32_t(m)) {
-    uint32_t prefix = L.misc[0] << 21, mask = 0xFFE00000u, need = L.misc[1];
-    const bool use_list = L.misc[3] <= uint32_t(kMaxList);
-    if (use_list) {  // gather the keys of the threshold bin once; later passes read only them
-      for (int p = lo + lane; p < hi; p += kWave) {
+    need = uint32_t(m);
+    for (;;) {
+      const uint64_t width = uint64_t(hi) - lo + 1;
+      const int bits = 64 - __clzll(width - 1);  // bits spanned by the interval
+      const int shift = bits > 11 ? bits - 11 : 0;
+      for (int p = lo_p + lane; p < hi_p; p += kWave) {
         const uint32_t k = L.keys[p];
-        if (k > kKeyNegInf && (k & mask) == prefix) L.cand[atomicAdd(&L.misc[4], 1u)] = k;
+        if (k > kKeyNegInf && k >= lo && k <= hi) lds_inc(&L.hist[(k - lo) >> shift]);
       }
       __syncthreads();
-    }
-    const int nc = use_list ? int(L.misc[4]) : n;
-    const int cseg = (((nc + kNW - 1) / kNW) + 63) & ~63;
-    const int clo = w * cseg, chi = min(nc, clo + cseg);
-    const int shifts[2] = {10, 0};
-    const int bits[2] = {11, 10};
-    for (int pass = 0; pass < 2; ++pass) {
-      const int sh = shifts[pass];
-      const uint32_t dmask = (1u << bits[pass]) - 1u;
-      for (int p = clo + lane; p < chi; p += kWave) {
-        const uint32_t k = use_list ? L.cand[p] : L.keys[p];
-        if (k > kKeyNegInf && (k & mask) == prefix) atomicAdd(&L.hist[hbin(int((k >> sh) & dmask))], 1u);
+      // bins [128w, 128w+128): lane holds bins b0 = 128w + 2*lane and b0 + 1
+      const int b0 = kBinsPerWave * w + 2 * lane;
+      const uint32_t h0 = L.hist[b0], h1 = L.hist[b0 + 1];
+      L.hist[b0] = 0;
+      L.hist[b0 + 1] = 0;
+      const uint32_t s = h0 + h1;
+      const uint32_t incl = __ockl_wfscan_add_u32(s, true);
+      const uint32_t wtot = uint32_t(__builtin_amdgcn_readlane(int(incl), kWave - 1));
+      if (lane == 0) L.wred[w] = wtot;
+      __syncthreads();
+      // keys in the bins of higher waves, then of higher lanes of this wave
+      const uint32_t v = lane < kNW ? L.wred[kNW - 1 - lane] : 0u;  // from the top wave down
+      const uint32_t incl_rev = __ockl_wfscan_add_u32(v, true);
+      const uint32_t above_w = w == kNW - 1 ? 0u : uint32_t(__builtin_amdgcn_readlane(int(incl_rev), kNW - 2 - w));
+      uint32_t above = above_w + (wtot - incl);
+      if (above < need && need <= above + s) {
+        if (need <= above + h1) {
+          L.misc[0] = uint32_t(b0 + 1);
+          L.misc[1] = need - above;
+        } else {
+          L.misc[0] = uint32_t(b0);
+          L.misc[1] = need - above - h1;
+        }
       }
       __syncthreads();
-      if (w == 0) find_digit(L, 1 << bits[pass], need);
-      __syncthreads();
-      prefix |= L.misc[0] << sh;
-      mask |= dmask << sh;
+      const uint32_t bin = L.misc[0];
       need = L.misc[1];
       __syncthreads();
+      const uint64_t new_lo = uint64_t(lo) + (uint64_t(bin) << shift);
+      hi = uint32_t(min(uint64_t(hi), new_lo + (uint64_t(1) << shift) - 1));
+      lo = uint32_t(new_lo);
+      if (shift == 0) break;  // a single key value: the threshold
     }
-    T = prefix;
-    need_eq = need;
+    T = lo;
   }
 
-  // per-wave counts of keys above and equal to the threshold
+  // order-preserving compaction: ties at T go to the lowest positions
   uint32_t gt = 0, eq = 0;
-  for (int p = lo + lane; p < hi; p += kWave) {
+  for (int p = lo_p + lane; p < hi_p; p += kWave) {
     const uint32_t k = L.keys[p];
     gt += k > T;
     eq += (k == T) && (k > kKeyNegInf);
   }
-  for (int off = 32; off > 0; off >>= 1) {
-    gt += __shfl_xor(gt, off, kWave);
-    eq += __shfl_xor(eq, off, kWave);
-  }
+  gt = __ockl_wfred_add_u32(gt);
+  eq = __ockl_wfred_add_u32(eq);
   if (lane == 0) {
-    L.wsum[w] = gt;
-    L.wsum[kNW + w] = eq;
+    L.wred[w] = gt;
+    L.wred[kNW + w] = eq;
   }
   __syncthreads();
-  uint32_t eq_base = 0, sel_base = 0, cum_eq = 0, chosen = 0;
-  for (int x = 0; x < kNW; ++x) {
-    if (x == w) {
-      eq_base = cum_eq;
-      sel_base = chosen;
-    }
-    const uint32_t e = L.wsum[kNW + x];
-    const uint32_t take = need_eq > cum_eq ? min(e, need_eq - cum_eq) : 0u;
-    chosen += L.wsum[x] + take;
-    cum_eq += e;
-  }
-  // order-preserving compaction inside the wave's segment
+  const uint32_t eq_base = waves_before(L, kNW, w);
+  const uint32_t take_w = need > eq_base ? min(eq, need - eq_base) : 0u;
+  if (lane == 0) L.wred[2 * kNW + w] = gt + take_w;
+  __syncthreads();
+  const uint32_t sel_base = waves_before(L, 2 * kNW, w);
+  const uint32_t chosen = reduce_waves(L, 2 * kNW, 0);
+  const uint64_t ltm = (uint64_t(1) << lane) - 1;
   uint32_t run_eq = 0, run_sel = 0;
-  for (int base = lo; base < lo + seg; base += kWave) {
+  for (int base = lo_p; base < lo_p + seg; base += kWave) {
     const int p = base + lane;
-    const uint32_t k = p < hi ? L.keys[p] : 0u;
-    const bool is_gt = k > T;
+    const uint32_t k = p < hi_p ? L.keys[p] : 0u;
     const bool is_eq = (k == T) && (k > kKeyNegInf);
     const uint64_t eqm = __ballot(is_eq);
-    const uint32_t eq_rank = eq_base + run_eq + __popcll(eqm & lanemask_lt());
-    const bool sel = is_gt || (is_eq && eq_rank < need_eq);
+    const bool sel = k > T || (is_eq && eq_base + run_eq + __popcll(eqm & ltm) < need);
     const uint64_t selm = __ballot(sel);
-    if (sel) out[sel_base + run_sel + __popcll(selm & lanemask_lt())] = uint32_t(p);
+    if (sel) out[sel_base + run_sel + __popcll(selm & ltm)] = uint32_t(p);
     run_eq += __popcll(eqm);
     run_sel += __popcll(selm);
   }
@@ -183,7 +196,11 @@ __device__ int select_top(const SelLds& L, int n, int m, uint32_t* out) {
   return int(chosen);
 }
 
-__device__ __forceinline__ uint32_t key_at(const float* a, int64_t i) { return score_key(a[i]); }
+// Key of a[i]; an index outside [0, n) (never produced by a correct
+// selection) reads nothing and counts as an invalid slot.
+__device__ __forceinline__ uint32_t key_in(const float* a, int64_t i, int64_t n) {
+  return (i >= 0 && i < n) ? score_key(a[i]) : kKeyNegInf;
+}
 
 __global__ __launch_bounds__(kNT) void select_kernel(int topk, int cand_blocks, int ratio, int64_t capacity,
                                                      const int32_t* __restrict__ q_pos, int n_q,
@@ -193,20 +210,21 @@ __global__ __launch_bounds__(kNT) void select_kernel(int topk, int cand_blocks, 
                                                      const float* __restrict__ sbmax, int64_t dom_cap,
                                                      int32_t* __restrict__ topk_out, int32_t* __restrict__ pool_out,
                                                      float* __restrict__ topk_scores) {
-  extern __shared__ uint32_t lds[];
+  extern __shared__ uint32_t lds_raw[];
+  lds_u32* lds = (lds_u32*)lds_raw;  // address-space cast into LDS
   SelLds L;
   L.keys = lds;
   L.la = L.keys + kMaxCand;
   L.lb = L.la + kMaxList;
-  L.cand = L.lb + kMaxList;
-  L.hist = L.cand + kMaxList;
-  L.wsum = L.hist + kHistWords;
-  L.misc = L.wsum + 2 * kNW;
-  for (int x = threadIdx.x; x < kHistWords; x += kNT) L.hist[x] = 0;
+  L.hist = L.lb + kMaxList;
+  L.wred = L.hist + kBins;
+  L.misc = L.wred + 4 * kNW;
+  for (int x = threadIdx.x; x < kBins; x += kNT) L.hist[x] = 0;
 
   const int qi = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int64_t row = int64_t(b) * n_q + qi;
-  const int64_t nsb = dom_cap / 64, nb = dom_cap / 8;
+  const int nsb = int(dom_cap / 64);
+  const int64_t nb = dom_cap / 8;
   const float* sc = scores + row * dom_cap;
   const float* bm = bmax + row * nb;
   const float* sbm = sbmax + row * nsb;
@@ -217,50 +235,63 @@ __global__ __launch_bounds__(kNT) void select_kernel(int topk, int cand_blocks, 
     const int64_t n_vis = visible_count(n, q_pos[row], ratio);
     const int64_t fb = n_vis > 0 ? (n_vis - 1) / 8 : -1;
     const int64_t fsb = fb >= 0 ? fb / 8 : -1;
-    for (int64_t p = tid; p < nsb; p += kNT) L.keys[p] = p == fsb ? kKeyForced : key_at(sbm, p);
-    __syncthreads();
-    const int na = select_top(L, int(nsb), cand_blocks, L.la);
+    int na = nsb;
+    if (nsb > cand_blocks) {
+      for (int p = tid; p < nsb; p += kNT) L.keys[p] = p == fsb ? kKeyForced : key_in(sbm, p, nsb);
+      __syncthreads();
+      na = select_top(L, nsb, cand_blocks, L.la);
+    } else {
+      for (int p = tid; p < nsb; p += kNT) L.la[p] = uint32_t(p);
+      __syncthreads();  // la is read across threads below
+    }
     for (int p = tid; p < 8 * na; p += kNT) {
       const int64_t blk = int64_t(L.la[p >> 3]) * 8 + (p & 7);
-      L.keys[p] = blk == fb ? kKeyForced : key_at(bm, blk);
+      L.keys[p] = blk == fb ? kKeyForced : key_in(bm, blk, nb);
     }
     __syncthreads();
     const int nbsel = select_top(L, 8 * na, cand_blocks, L.lb);
     for (int x = tid; x < cand_blocks; x += kNT) {
       int32_t v = -1;
-      if (x < nbsel) v = int32_t(int64_t(L.la[L.lb[x] >> 3]) * 8 + (L.lb[x] & 7));
+      if (x < nbsel) v = int32_t(min(int64_t(L.la[L.lb[x] >> 3]) * 8 + (L.lb[x] & 7), nb - 1));
       pool_out[row * cand_blocks + x] = v;
     }
     __syncthreads();
   }
 
   // ---- top-k entries ----
-  for (int64_t p = tid; p < nsb; p += kNT) L.keys[p] = key_at(sbm, p);
-  __syncthreads();
-  const int na = select_top(L, int(nsb), topk, L.la);
-  for (int p = tid; p < 8 * na; p += kNT) L.keys[p] = key_at(bm, int64_t(L.la[p >> 3]) * 8 + (p & 7));
+  int na = nsb;
+  if (nsb > topk) {
+    for (int p = tid; p < nsb; p += kNT) L.keys[p] = key_in(sbm, p, nsb);
+    __syncthreads();
+    na = select_top(L, nsb, topk, L.la);
+  } else {
+    for (int p = tid; p < nsb; p += kNT) L.la[p] = uint32_t(p);
+    __syncthreads();  // la is read across threads below
+  }
+  for (int p = tid; p < 8 * na; p += kNT) L.keys[p] = key_in(bm, int64_t(L.la[p >> 3]) * 8 + (p & 7), nb);
   __syncthreads();
   const int nbsel = select_top(L, 8 * na, topk, L.lb);
   // block ids of the chosen blocks (ascending)
   for (int x = tid; x < nbsel; x += kNT) L.lb[x] = L.la[L.lb[x] >> 3] * 8 + (L.lb[x] & 7);
   __syncthreads();
-  for (int p = tid; p < 8 * nbsel; p += kNT) L.keys[p] = key_at(sc, int64_t(L.lb[p >> 3]) * 8 + (p & 7));
+  for (int p = tid; p < 8 * nbsel; p += kNT) L.keys[p] = key_in(sc, int64_t(L.lb[p >> 3]) * 8 + (p & 7), dom_cap);
   __syncthreads();
   const int ne = select_top(L, 8 * nbsel, topk, L.la);
   for (int x = tid; x < topk; x += kNT) {
     int32_t id = -1;
     float s = -INFINITY;
     if (x < ne) {
-      const int64_t slot = int64_t(L.lb[L.la[x] >> 3]) * 8 + (L.la[x] & 7);
+      const int64_t slot = min(int64_t(L.lb[L.la[x] >> 3]) * 8 + (L.la[x] & 7), dom_cap - 1);
       s = sc[slot];
-      id = pool_in ? int32_t(int64_t(pool_in[row * cand_blocks + slot / 8]) * 8 + (slot & 7)) : int32_t(slot);
+      id = pool_in ? int32_t(int64_t(pool_in[row * cand_blocks + min(slot / 8, int64_t(cand_blocks) - 1)]) * 8 + (slot & 7))
+                   : int32_t(slot);
     }
     topk_out[row * topk + x] = id;
     if (topk_scores) topk_scores[row * topk + x] = s;
   }
 }
 
-constexpr size_t kSelectLds = sizeof(uint32_t) * (kMaxCand + 3 * kMaxList + kHistWords + 2 * kNW + 8);
+constexpr size_t kSelectLds = sizeof(uint32_t) * (kMaxCand + 2 * kMaxList + kBins + 4 * kNW + 8);
 
 }  // namespace
 
