@@ -89,3 +89,64 @@ def run_step(inp, seqs=None, caches=None):
     n_entries = [c.n_entries for c in out_caches]
     results = csa2.run_group(dims, out_caches, n_entries, q_pos, layer_specs(inp, seqs))
     return results, out_caches
+
+
+class LazyMainCache(csa2.SeqCache):
+    """A sequence cache whose indexer K is stored in full but whose main-KV
+    rows are made (compressed, rotated, stored) only when a row is read.
+
+    Same arithmetic as build_cache; it only defers the main-KV rows, which a
+    step reads for the few kept entries, so very long contexts fit in memory.
+    """
+
+    def __init__(self, inp, b: int, stop_pos: int, chunk: int = 1 << 14):
+        wl = inp.wl
+        super().__init__(wl.kv, wl.main_group, wl.idx_group, {}, {})
+        self.inp, self.b = inp, b
+        self._n = stop_pos // wl.ratio
+        logits, w_ik = inp.pair_logits(), inp.w_ik()
+        chunk -= chunk % wl.ratio
+        for p0 in range(0, stop_pos, chunk):
+            p1 = min(stop_pos, p0 + chunk)
+            e = csa2.compress(inp.latent(b, p0, p1), logits, wl.ratio)
+            j = p0 // wl.ratio + np.arange(e.shape[0])
+            e_hat = csa2.rope(e, csa2.entry_position(j, wl.ratio), wl.d_rope, wl.rope_theta)
+            _, idx_raw = formats_store(e_hat @ np.asarray(w_ik, dtype=np.float64), wl.kv, wl.idx_group)
+            for key, arr in idx_raw.items():
+                self.idx_raw.setdefault(key, []).append(arr)
+        self.idx_raw = {k: np.concatenate(v) for k, v in self.idx_raw.items()}
+
+    @property
+    def n_entries(self) -> int:
+        return self._n
+
+    def main_raw_rows(self, ids, fetch: int = 4096) -> dict:
+        """Raw stored main-KV parts of the given entries (latent read in aligned runs of `fetch` positions)."""
+        wl = self.inp.wl
+        ids = np.asarray(ids, dtype=np.int64)
+        fetch -= fetch % wl.ratio
+        rows = {}
+        for blk in np.unique(ids * wl.ratio // fetch):
+            p0 = int(blk) * fetch
+            sel = ids[(ids * wl.ratio // fetch) == blk]
+            lat = self.inp.latent(self.b, p0, p0 + fetch)
+            for j in np.unique(sel):
+                q0 = int(j) * wl.ratio - p0
+                e = csa2.compress(lat[q0 : q0 + wl.ratio], self.inp.pair_logits(), wl.ratio)
+                e_hat = csa2.rope(e, csa2.entry_position(np.array([j]), wl.ratio), wl.d_rope, wl.rope_theta)
+                rows[int(j)] = formats_store(e_hat, wl.kv, wl.main_group)[1]
+        keys = rows[int(ids[0])].keys() if len(ids) else []
+        return {k: np.concatenate([rows[int(j)][k] for j in ids]) for k in keys}
+
+    def main_rows(self, ids) -> np.ndarray:
+        ids = np.asarray(ids, dtype=np.int64)
+        if len(ids) == 0:
+            return np.zeros((0, self.inp.wl.d))
+        raw = self.main_raw_rows(ids)
+        return self._decode(raw, np.arange(len(ids)), self.main_group)
+
+
+def formats_store(x, fmt, group):
+    from . import formats
+
+    return formats.store(x, fmt, group)

@@ -112,8 +112,9 @@ def check_outputs(got, ref, wl, what=""):
     return err, rl2
 
 
-def check_step(step, inp, seqs=None, caches=None):
-    """Full parity of one executed GPU step against the oracle on sequences seqs.
+def check_step(step, inp, seqs=None, caches=None, queries=None):
+    """Full parity of one executed GPU step against the oracle on sequences seqs
+    (and query indices `queries`, default all).
 
     Returns a summary dict (counts of tie-band differences, worst errors).
     """
@@ -132,7 +133,7 @@ def check_step(step, inp, seqs=None, caches=None):
         lse = L["lse"].cpu().numpy()
         for i, b in enumerate(seqs):
             cache = caches[i]
-            for qi in range(wl.n_q):
+            for qi in (range(wl.n_q) if queries is None else queries):
                 t = int(q_pos[b, qi])
                 tag = f"{wl.name} layer {li} ({plan.mode}) seq {b} q {qi}"
                 n_vis = oc.visible_entries(cache.n_entries, t, wl.ratio)
@@ -156,3 +157,25 @@ def check_step(step, inp, seqs=None, caches=None):
                 summary["rel_l2"] = max(summary["rel_l2"], rl2)
                 assert np.allclose(lse[b, qi], ls, atol=2e-2 if wl.act == "bf16" else 1e-5), f"{tag}: lse"
     return summary
+
+
+def compare_cache_rows(step, cache, b, ids):
+    """GPU-written rows `ids` of sequence b vs the oracle's stored bytes (main KV and indexer K): exact."""
+    wl = step.wl
+    ids = np.asarray(ids, dtype=np.int64)
+    main_ref = cache.main_raw_rows(ids) if hasattr(cache, "main_raw_rows") else {k: v[ids] for k, v in cache.main_raw.items()}
+    idx_ref = {k: v[ids] for k, v in cache.idx_raw.items()}
+    t_ids = torch.from_numpy(ids).to(step.cache.main.device)
+    if wl.kv == "fp4":
+        pairs = [(step.cache.main[b][t_ids], main_ref["codes"]), (step.cache.main_scale[b][t_ids], main_ref["scales"]),
+                 (step.cache.idx[b][t_ids], idx_ref["codes"]), (step.cache.idx_scale[b][t_ids], idx_ref["scales"])]
+        for got, ref in pairs:
+            bad = np.count_nonzero(got.cpu().numpy() != ref)
+            assert bad == 0, f"seq {b}: {bad} FP4 bytes differ on sampled rows"
+    else:
+        key = "bf16" if wl.kv == "bf16" else "f32"
+        for got, ref in ((step.cache.main[b][t_ids], main_ref[key]), (step.cache.idx[b][t_ids], idx_ref[key])):
+            g = got.cpu()
+            g = g.view(torch.int16).numpy().view(np.uint16) if key == "bf16" else g.numpy()
+            bad = np.count_nonzero(g != ref)
+            assert bad == 0, f"seq {b}: {bad} {key} elements differ on sampled rows"
