@@ -173,6 +173,15 @@ __device__ __forceinline__ void dequant_fp4_32(uint4 codes, float s0, float s1, 
 
 __device__ __forceinline__ int acc_row(int i, int half) { return 8 * (i >> 2) + 4 * half + (i & 3); }
 
+// Value of v held by lane src (lower half) or src + 4 (upper half): the head
+// of accumulator row acc_row(i, half).  Two uniform readlanes and a select
+// instead of a cross-lane LDS permute.
+__device__ __forceinline__ float lane_value(float v, int src, int half) {
+  const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src));
+  const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src + 4));
+  return half ? hi : lo;
+}
+
 template <bool FP4>
 __global__ __launch_bounds__(256) void attn_mfma_kernel(
     int H, int topk, int window, int main_group, int d_rope, int64_t capacity, RopeTable rope,
@@ -316,7 +325,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
     m_run = m_new;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float a = __shfl(alpha, acc_row(i, h), kWave);
+      const float a = lane_value(alpha, acc_row(i, 0), h);
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) oacc[cb][i] *= a;
     }
@@ -341,7 +350,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int hh = acc_row(i, h);
-      const float lh = __shfl(l_run, hh, kWave);
+      const float lh = lane_value(l_run, acc_row(i, 0), h);
       const float inv = lh > 0.0f ? 1.0f / lh : 0.0f;
       uint16_t* orow = out + (bq * H + hg * 32 + hh) * kD + 128 * wave + n;
 #pragma unroll
@@ -363,29 +372,45 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
   }
 }
 
-// Combine the split partials of one (query, head): weights exp(m_s - M).
-__global__ __launch_bounds__(256) void attn_merge_kernel(int H, int n_splits, const float* __restrict__ part_o,
+// Combine the split partials of one (query, head): weights exp(m_s - M) / L,
+// computed once by one wave, then each thread adds four channels of every
+// split with 16-byte loads.
+extern "C" __device__ float __ockl_wfred_max_f32(float);
+extern "C" __device__ float __ockl_wfred_add_f32(float);
+
+constexpr int kMaxSplits = 64;
+
+__global__ __launch_bounds__(128) void attn_merge_kernel(int H, int n_splits, const float* __restrict__ part_o,
                                                          const float* __restrict__ part_ml,
                                                          uint16_t* __restrict__ out, float* __restrict__ lse) {
-  const int head = blockIdx.x;
+  __shared__ float wgt[kMaxSplits];
+  const int head = blockIdx.x, tid = threadIdx.x;
   const int64_t bq = blockIdx.y;
-  float M = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, part_ml[((bq * n_splits + s) * H + head) * 2]);
-  float L = 0.0f;
-  for (int s = 0; s < n_splits; ++s) {
-    const float ms = part_ml[((bq * n_splits + s) * H + head) * 2];
-    if (ms > -INFINITY) L += __expf(ms - M) * part_ml[((bq * n_splits + s) * H + head) * 2 + 1];
+  if (tid < kWave) {
+    const int64_t at = ((bq * n_splits + tid) * H + head) * 2;
+    const float m = tid < n_splits ? part_ml[at] : -INFINITY;
+    const float l = tid < n_splits ? part_ml[at + 1] : 0.0f;
+    const float M = __ockl_wfred_max_f32(m);
+    const float e = m > -INFINITY ? __expf(m - M) : 0.0f;
+    const float L = __ockl_wfred_add_f32(e * l);
+    if (tid < n_splits) wgt[tid] = L > 0.0f ? e / L : 0.0f;
+    if (lse && tid == 0) lse[bq * H + head] = L > 0.0f ? M + logf(L) : -INFINITY;
   }
-  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  for (int c = threadIdx.x; c < kD; c += blockDim.x) {
-    float acc = 0.0f;
-    for (int s = 0; s < n_splits; ++s) {
-      const float ms = part_ml[((bq * n_splits + s) * H + head) * 2];
-      if (ms > -INFINITY) acc += __expf(ms - M) * part_o[((bq * n_splits + s) * H + head) * kD + c];
-    }
-    out[(bq * H + head) * kD + c] = f32_to_bf16(acc * inv);
+  __syncthreads();
+  const int c = 4 * tid;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int sp = 0; sp < n_splits; ++sp) {
+    const float wv = wgt[sp];
+    const float4 v = *reinterpret_cast<const float4*>(part_o + ((bq * n_splits + sp) * H + head) * kD + c);
+    acc.x += wv * v.x;
+    acc.y += wv * v.y;
+    acc.z += wv * v.z;
+    acc.w += wv * v.w;
   }
-  if (lse && threadIdx.x == 0) lse[bq * H + head] = L > 0.0f ? M + logf(L) : -INFINITY;
+  uint2 packed;
+  packed.x = uint32_t(f32_to_bf16(acc.x)) | (uint32_t(f32_to_bf16(acc.y)) << 16);
+  packed.y = uint32_t(f32_to_bf16(acc.z)) | (uint32_t(f32_to_bf16(acc.w)) << 16);
+  *reinterpret_cast<uint2*>(out + (bq * H + head) * kD + c) = packed;
 }
 
 struct AttnPlan {
@@ -404,6 +429,7 @@ AttnPlan plan_attn(const csa2_dims& dims, const csa2_kv_cache& cache, int32_t n_
   const int64_t units = int64_t(cache.batch) * n_q * (dims.n_heads / 32);
   int splits = int(units >= 512 ? 1 : (512 + units - 1) / units);
   splits = splits < 1 ? 1 : (splits > p.n_tiles ? p.n_tiles : splits);
+  splits = splits > kMaxSplits ? kMaxSplits : splits;
   p.tiles_per_split = (p.n_tiles + splits - 1) / splits;
   p.n_splits = (p.n_tiles + p.tiles_per_split - 1) / p.tiles_per_split;
   return p;
@@ -440,7 +466,7 @@ hipError_t launch_attn(const csa2_dims& dims, const csa2_kv_cache& cache, const 
                        p.n_splits, static_cast<uint16_t*>(out), lse, part_o, part_ml);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_splits == 1) return e;
-    hipLaunchKernelGGL(attn_merge_kernel, dim3(dims.n_heads, unsigned(int64_t(cache.batch) * n_q)), dim3(256), 0,
+    hipLaunchKernelGGL(attn_merge_kernel, dim3(dims.n_heads, unsigned(int64_t(cache.batch) * n_q)), dim3(128), 0,
                        stream, dims.n_heads, p.n_splits, part_o, part_ml, static_cast<uint16_t*>(out), lse);
     return hipGetLastError();
   }

@@ -19,7 +19,7 @@
 namespace csa2 {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;
 
 // Store `n` float64 values as one cache row of the given format.
 __device__ void store_row(const double* v, int n, int dtype, int group, void* base, uint8_t* scale_base, int64_t row) {
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
 
   // 4. indexer K = e_hat . W_ik, from the unrounded rotated entry.  Thread
   // (part, pair) sums output channels 2*pair, 2*pair+1 over a slice of the
-  // input channels; W_ik rows are read as contiguous pairs, 64 loads in
+  // input channels; W_ik rows are read as contiguous pairs, 32 loads in
   // flight before the FMAs (this kernel is latency-bound, not
   // bandwidth-bound); the float64 partials are added through LDS.
   {
@@ -124,10 +124,10 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
       for (int p0 = pair; p0 < pairs; p0 += kThreads) {
         a0 = a1 = 0.0;
         int c = c_lo;
-        for (; c + 64 <= c_hi; c += 64) {
-          float w0[64], w1[64];
+        for (; c + 32 <= c_hi; c += 32) {
+          float w0[32], w1[32];
 #pragma unroll
-          for (int u = 0; u < 64; ++u) {
+          for (int u = 0; u < 32; ++u) {
             const int64_t off = int64_t(c + u) * d_idx + 2 * p0;
             if constexpr (ACT_BF16) {
               const uint32_t two = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(w_ik) + off);
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
             }
           }
 #pragma unroll
-          for (int u = 0; u < 64; ++u) {
+          for (int u = 0; u < 32; ++u) {
             a0 += e[c + u] * double(w0[u]);
             a1 += e[c + u] * double(w1[u]);
           }

@@ -119,7 +119,7 @@ __device__ __forceinline__ bf16x8_t fp4x8_to_bf16(uint32_t w) {
 }
 
 template <bool FP4>
-__global__ __launch_bounds__(256, 2) void scan_mfma_kernel(
+__device__ __forceinline__ void scan_mfma_body(
     int ratio, int64_t capacity, const uint16_t* __restrict__ idx_q, const float* __restrict__ head_w,
     const int32_t* __restrict__ q_pos, int n_q, const int32_t* __restrict__ pool_in, int cand_blocks,
     const uint8_t* __restrict__ idx_k, const uint8_t* __restrict__ idx_scale, const int32_t* __restrict__ n_entries,
@@ -235,6 +235,26 @@ __global__ __launch_bounds__(256, 2) void scan_mfma_kernel(
   }
 }
 
+// bf16 keeps one tile pair in flight per wave and fits 3 waves per SIMD;
+// FP4 keeps four pairs in flight (its rows are a quarter the size) at 2.
+__global__ __launch_bounds__(256, 3) void scan_mfma_bf16_kernel(
+    int ratio, int64_t capacity, const uint16_t* __restrict__ idx_q, const float* __restrict__ head_w,
+    const int32_t* __restrict__ q_pos, int n_q, const int32_t* __restrict__ pool_in, int cand_blocks,
+    const uint8_t* __restrict__ idx_k, const uint8_t* __restrict__ idx_scale, const int32_t* __restrict__ n_entries,
+    float* __restrict__ scores, float* __restrict__ bmax, float* __restrict__ sbmax, int64_t dom_cap) {
+  scan_mfma_body<false>(ratio, capacity, idx_q, head_w, q_pos, n_q, pool_in, cand_blocks, idx_k, idx_scale, n_entries,
+                        scores, bmax, sbmax, dom_cap);
+}
+
+__global__ __launch_bounds__(256, 2) void scan_mfma_fp4_kernel(
+    int ratio, int64_t capacity, const uint16_t* __restrict__ idx_q, const float* __restrict__ head_w,
+    const int32_t* __restrict__ q_pos, int n_q, const int32_t* __restrict__ pool_in, int cand_blocks,
+    const uint8_t* __restrict__ idx_k, const uint8_t* __restrict__ idx_scale, const int32_t* __restrict__ n_entries,
+    float* __restrict__ scores, float* __restrict__ bmax, float* __restrict__ sbmax, int64_t dom_cap) {
+  scan_mfma_body<true>(ratio, capacity, idx_q, head_w, q_pos, n_q, pool_in, cand_blocks, idx_k, idx_scale, n_entries,
+                       scores, bmax, sbmax, dom_cap);
+}
+
 }  // namespace
 
 hipError_t launch_scan(const csa2_dims& dims, const csa2_kv_cache& cache, const void* idx_q, const float* head_w,
@@ -245,7 +265,7 @@ hipError_t launch_scan(const csa2_dims& dims, const csa2_kv_cache& cache, const 
   if (mfma_shape) {
     const int64_t nsb = ss.dom_cap / 64;
     const dim3 grid(unsigned((nsb + 4 * kSbPerWave - 1) / (4 * kSbPerWave)), n_q, cache.batch);
-    auto kern = cache.kv_dtype == CSA2_FP4 ? scan_mfma_kernel<true> : scan_mfma_kernel<false>;
+    auto kern = cache.kv_dtype == CSA2_FP4 ? scan_mfma_fp4_kernel : scan_mfma_bf16_kernel;
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, cache.ratio, cache.capacity,
                        static_cast<const uint16_t*>(idx_q), head_w, q_pos, n_q, pool_in, dims.cand_blocks,
                        static_cast<const uint8_t*>(cache.idx_k), cache.idx_scale, cache.n_entries, ss.scores, ss.bmax,
