@@ -10,14 +10,22 @@ in HBM when timing starts.  Several identical copies of the cache are rotated
 step by step so that no step finds the previous step's data in the 256 MB
 Infinity Cache.
 
-Prints one JSON line: whole-step decode tokens/s, the roofline of the
-dominant kernel (the indexer scan+select call, timed with HIP events on the
-launch stream), and the float64 CPU oracle timed on a bounded sample of the
+The timed steps replay HIP graphs captured from the library's calls (one
+graph per cache copy; --eager launches them directly).  The same steps are
+then run again with the library's kernel trace on, which brackets every
+kernel with HIP events on its launch stream; the roofline is that of the
+dominant kernel, the full-domain indexer scan: algorithmic HBM bytes per
+launch over its mean duration for decode (one query per sequence), MFMA
+flops per launch for prefill (many queries share each sequence's K).
+
+Prints one JSON line: whole-step tokens/s, the per-kernel device times, the
+scan roofline, and the float64 CPU oracle timed on a bounded sample of the
 same workload on the host cores.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -30,28 +38,86 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD public figure
 METRIC = "CSA2 decode tokens/s and achieved HBM GB/s (% peak) at 32K–1M context"
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, AMD public figure
+
+
 def entry_bytes(width: int, kv: str, group: int) -> float:
     if kv == "fp4":
         return width / 2 + width / group
     return width * (2 if kv == "bf16" else 4)
 
 
+def visible_counts(wl):
+    """Visible cache entries of each query position (the same for every sequence)."""
+    import numpy as np
+
+    t = wl.q_positions()[0].astype(np.int64)
+    return np.minimum(wl.capacity, (t + 1) // wl.ratio)
+
+
+def scan_work(wl) -> dict:
+    """Algorithmic work of one full-domain indexer scan launch: every sequence's
+    visible indexer K read once, the queries and head weights read once; the
+    MFMA flops of the score contraction (one multiply-add per head, channel
+    and (query, visible entry) pair)."""
+    act = 2 if wl.act == "bf16" else 4
+    n_vis = visible_counts(wl)
+    idx_b = entry_bytes(wl.d_idx, wl.kv, wl.idx_group)
+    k_bytes = wl.batch * int(n_vis.max()) * idx_b
+    q_bytes = wl.batch * wl.n_q * wl.n_idx_heads * (wl.d_idx * act + 4)
+    flops = 2 * wl.n_idx_heads * wl.d_idx * wl.batch * int(n_vis.sum())
+    return {"bytes": float(k_bytes + q_bytes), "flops": float(flops)}
+
+
 def algorithmic_bytes(wl) -> dict:
-    """Bytes the method must move per step, by stage (no scratch, no re-reads)."""
+    """Bytes the method must move per step, by stage (no scratch, no re-reads):
+    each sequence's indexer K is read once, each query gathers its kept rows."""
     act = 2 if wl.act == "bf16" else 4
     main_b = entry_bytes(wl.d, wl.kv, wl.main_group)
     idx_b = entry_bytes(wl.d_idx, wl.kv, wl.idx_group)
     nq = wl.batch * wl.n_q
     n_new = wl.new // wl.ratio
     compress = wl.batch * (wl.new * wl.d * act + n_new * (main_b + idx_b)) + wl.d * wl.d_idx * act
-    t_last = wl.context - 1
-    n_vis = min(wl.capacity, (t_last + 1) // wl.ratio)
-    index = wl.batch * wl.n_q * n_vis * idx_b + nq * (wl.n_idx_heads * wl.d_idx * act + wl.n_idx_heads * 4 + wl.topk * 4)
-    attn = nq * (wl.topk * (main_b + 4) + wl.window * wl.d * act + 2 * wl.n_heads * wl.d * act + wl.n_heads * 4)
+    index = scan_work(wl)["bytes"] + nq * wl.topk * 4
+    for p in wl.layers[1:]:
+        if p.mode == "reindex":  # pool-domain rescoring: the pool's entries per query
+            index += nq * (min(wl.cand_blocks * 8, wl.capacity) * idx_b + wl.n_idx_heads * (wl.d_idx * act + 4) + wl.topk * 4)
+    attn_one = nq * (wl.topk * (main_b + 4) + wl.window * wl.d * act + 2 * wl.n_heads * wl.d * act + wl.n_heads * 4)
+    attn = attn_one * len(wl.layers)
     return {"compress": compress, "index": index, "attn": attn, "total": compress + index + attn}
 
 
-def run_gpu(wl, steps: int, warmup: int, copies: int):
+# sources that define the scan kernels; a counter summary holds their digest
+SCAN_SOURCES = ("kv_cache_compression_csa2_amd/csrc/index_scan.hip",
+                "kv_cache_compression_csa2_amd/csrc/device_common.hpp")
+
+
+def sources_digest(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str, kernel: str):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's
+    counts) from the committed counter summary for this kernel and workload;
+    None if there is none, or if the kernel's sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("traffic: "):
+                rec = json.loads(line[len("traffic: "):])
+                if rec.get("sources_sha256") != sources_digest(SCAN_SOURCES):
+                    return None
+                return rec.get("bytes_per_launch")
+    return None
+
+
+def run_gpu(wl, steps: int, warmup: int, copies: int, use_graph: bool):
     import torch
 
     import synth
@@ -71,55 +137,58 @@ def run_gpu(wl, steps: int, warmup: int, copies: int):
         c.n_entries.copy_(step.cache.n_entries)
         caches.append(c)
     structs = [c.struct() for c in caches]
-    single_full = len(wl.layers) == 1 and wl.layers[0].mode == "full"
-    L = step.layers[0]
     ws = step.workspace()
-    ws_idx = ws
-    cargs = step.compress_args()
+    cargs = step.compress_args() if wl.new else None
+    layers = step.layer_structs()
 
-    def one(i, ev=None):
-        cs = structs[i % len(structs)]
-        if not single_full:
-            if ev:
-                ev[0].record()
-            B.csa2_layer_group(step.dims, cs, step.layer_structs(), step.q_pos, wl.n_q, cargs, ws)
-            if ev:
-                ev[3].record()
-            return
-        if ev:
-            ev[0].record()
-        if wl.new:
-            B.csa2_compress(step.dims, cs, step.latent_new, step.first_pos, wl.new, step.pair_logits, step.w_ik)
-        if ev:
-            ev[1].record()
-        B.csa2_index_topk(step.dims, cs, L["q_idx"], L["head_w"], step.q_pos, wl.n_q, None, L["topk"],
-                          L["pool"], None, ws_idx)
-        if ev:
-            ev[2].record()
-        B.csa2_sparse_attn(step.dims, cs, L["q"], step.q_pos, wl.n_q, L["topk"], L["swa"], L["swa_first"],
-                           L["swa"].shape[1], L["out"], L["lse"], ws)
-        if ev:
-            ev[3].record()
+    def one(i):
+        # one decode step on cache copy i: compress the new rows, then the layer group
+        B.csa2_layer_group(step.dims, structs[i % copies], layers, step.q_pos, wl.n_q, cargs, ws)
 
     for i in range(warmup):
         one(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    graphs = []
+    if use_graph:
+        for c in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                one(c)
+            graphs.append(g)
+        for c in range(copies):
+            graphs[c].replay()
+        torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps, nothing else enqueued
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        one(warmup + i, evs[i])
+        if graphs:
+            graphs[i % copies].replay()
+        else:
+            one(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    stages = {}
-    if single_full:
-        stages = {
-            "compress": sum(e[0].elapsed_time(e[1]) for e in evs) / steps,
-            "index_topk": sum(e[1].elapsed_time(e[2]) for e in evs) / steps,
-            "sparse_attn": sum(e[2].elapsed_time(e[3]) for e in evs) / steps,
-        }
-    stages["step_events"] = sum(e[0].elapsed_time(e[3]) for e in evs) / steps
-    return (t1 - t0) * 1e3 / steps, stages
+    ms = (t1 - t0) * 1e3 / steps
+
+    # the same steps again, launched directly with the library's kernel trace on:
+    # HIP events around every kernel, on the launch stream
+    B.csa2_trace_enable(64 * steps)
+    for i in range(steps):
+        one(i)
+    torch.cuda.synchronize()
+    recs, dropped = B.csa2_trace_read(64 * steps)
+    B.csa2_trace_enable(0)
+    if dropped or len(recs) % steps:
+        raise RuntimeError(f"kernel trace incomplete: {len(recs)} records, {dropped} dropped")
+    per_step = len(recs) // steps
+    launches = []  # (kernel, mean ms) for each launch position of a step
+    for j in range(per_step):
+        names = {recs[i * per_step + j][0] for i in range(steps)}
+        if len(names) != 1:
+            raise RuntimeError("steps launched different kernel sequences")
+        launches.append((recs[j][0], sum(recs[i * per_step + j][1] for i in range(steps)) / steps))
+    return ms, launches
 
 
 def cpu_baseline(wl, seconds: float) -> dict:
@@ -165,8 +234,11 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_32k")
     ap.add_argument("--copies", type=int, default=4, help="rotated cache copies (defeats the Infinity Cache)")
+    ap.add_argument("--eager", action="store_true", help="launch the timed steps directly instead of replaying HIP graphs")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the run, copy a buffer of this many MiB 5 times (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
@@ -176,16 +248,36 @@ def main() -> int:
 
     wl = synth.get(args.workload)
     print(f"[bench] {wl.name}: {wl.description}", file=sys.stderr, flush=True)
-    ms, stages = run_gpu(wl, args.steps, args.warmup, args.copies)
-    print(f"[bench] gpu done: {ms:.4f} ms/step, stages {stages}", file=sys.stderr, flush=True)
+    ms, launches = run_gpu(wl, args.steps, args.warmup, args.copies, not args.eager)
+    print(f"[bench] gpu done: {ms:.4f} ms/step; kernels (ms): "
+          + ", ".join(f"{k} {v:.4f}" for k, v in launches), file=sys.stderr, flush=True)
+    if args.copy_mib:
+        import torch
+
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: 5 copies of {args.copy_mib} MiB", file=sys.stderr, flush=True)
+
     nbytes = algorithmic_bytes(wl)
     tokens = wl.batch * wl.n_q
-    roof = None
-    if "index_topk" in stages:
-        achieved = nbytes["index"] / (stages["index_topk"] * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": "csa2_index_topk (indexer scan + select)", "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "bytes_per_launch": nbytes["index"], "avg_ms": round(stages["index_topk"], 5), "traffic": None}
+    work = scan_work(wl)
+    scan_ms = next(v for k, v in launches if k.startswith("scan_"))
+    scan_name = next(k for k, v in launches if k.startswith("scan_"))
+    if wl.n_q == 1:
+        achieved = work["bytes"] / (scan_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": scan_name, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "per_launch": work["bytes"],
+                "avg_ms": round(scan_ms, 5)}
+    else:
+        achieved = work["flops"] / (scan_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": scan_name, "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "per_launch": work["flops"],
+                "avg_ms": round(scan_ms, 5)}
+    roof["traffic"] = recorded_traffic(wl.name, scan_name)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, args.cpu_seconds)
@@ -197,12 +289,13 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.batch, "context": wl.context, "ratio": wl.ratio,
                    "kv": wl.kv, "heads": f"{wl.n_heads}x{wl.d}", "indexer": f"{wl.n_idx_heads}x{wl.d_idx}",
-                   "topk": wl.topk, "window": wl.window, "layers": [p.mode for p in wl.layers],
-                   "cache_copies": args.copies},
+                   "topk": wl.topk, "window": wl.window, "queries_per_seq": wl.n_q,
+                   "layers": [p.mode for p in wl.layers], "cache_copies": args.copies,
+                   "launch": "eager" if args.eager else "hip_graph"},
         "step_hbm_gbps": round(nbytes["total"] / (ms * 1e-3) / 1e9, 1),
         "step_hbm_frac": round(nbytes["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "step_bytes": nbytes["total"],
-        "stages_ms": {k: round(v, 5) for k, v in stages.items()},
+        "kernels_ms": [[k, round(v, 5)] for k, v in launches],
         "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

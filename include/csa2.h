@@ -261,6 +261,46 @@ const char* csa2_last_error(void);
 /* CSA2_ABI_VERSION of the loaded library. */
 int32_t csa2_abi_version(void);
 
+/* ---------------------------------------------------------- kernel trace --
+ * Optional timing of every kernel the library launches, for profiling.  When
+ * enabled, each launch carries a start and a stop HIP event that the runtime
+ * stamps with the kernel's own start and end times on the device, so a
+ * record's time is that kernel's duration, in launch order.  Off by default;
+ * the entry points then launch plainly.  Not for use under stream capture. */
+typedef enum csa2_kernel {
+  CSA2_KERNEL_COMPRESS = 1,       /* compress_kernel (both activation types) */
+  CSA2_KERNEL_SCAN_GENERIC = 2,   /* scan_generic_kernel */
+  CSA2_KERNEL_SCAN_BF16 = 3,      /* scan_mfma_bf16_kernel */
+  CSA2_KERNEL_SCAN_FP4 = 4,       /* scan_mfma_fp4_kernel */
+  CSA2_KERNEL_SELECT = 5,         /* select_kernel */
+  CSA2_KERNEL_ATTN_GENERIC = 6,   /* attn_generic_kernel */
+  CSA2_KERNEL_ATTN_BF16 = 7,      /* attn_mfma_kernel over a bf16 cache */
+  CSA2_KERNEL_ATTN_FP4 = 8,       /* attn_mfma_kernel over an FP4 cache */
+  CSA2_KERNEL_ATTN_MERGE = 9      /* attn_merge_kernel */
+} csa2_kernel;
+
+typedef struct csa2_trace_record {
+  int32_t kernel; /* csa2_kernel */
+  float ms;       /* the kernel's duration on the device */
+} csa2_trace_record;
+
+/* Enable tracing of up to max_kernels launches (creating 2 * max_kernels HIP
+ * events on the current device, which launches must then target), or disable
+ * it and free the events when max_kernels is 0.  Drops any unread records.
+ * Launches beyond max_kernels before the next read are not recorded and are
+ * counted as dropped.  Returns a csa2_status. */
+int csa2_trace_enable(int32_t max_kernels);
+
+/* Wait for the recorded launches to finish and copy up to `max` records, in
+ * launch order, into host array `out`; then start a new recording.  Returns
+ * the number of records copied (>= 0) or a negative csa2_status.  If n_dropped
+ * is not NULL it receives the number of launches not recorded (beyond the
+ * capacity, or beyond `max`). */
+int csa2_trace_read(csa2_trace_record* out, int32_t max, int32_t* n_dropped);
+
+/* Static name of a csa2_kernel: the name of its __global__ function. */
+const char* csa2_kernel_name(int32_t kernel);
+
 #ifdef __cplusplus
 }
 #endif

@@ -57,6 +57,10 @@ class Layer(ctypes.Structure):
     ]
 
 
+class TraceRecord(ctypes.Structure):
+    _fields_ = [("kernel", c_int32), ("ms", ctypes.c_float)]
+
+
 class CompressArgs(ctypes.Structure):
     _fields_ = [
         ("latent", c_void_p), ("first_pos", c_void_p), ("n_pos", c_int32), ("reserved0", c_int32),
@@ -85,9 +89,16 @@ _lib.csa2_sparse_attn.argtypes = [POINTER(Dims), POINTER(KVCache), c_void_p, c_v
 _lib.csa2_layer_group.restype = c_int
 _lib.csa2_layer_group.argtypes = [POINTER(Dims), POINTER(KVCache), c_int32, POINTER(Layer), c_void_p, c_int32,
                                   POINTER(CompressArgs), c_void_p, c_size_t, c_void_p]
+_lib.csa2_trace_enable.restype = c_int
+_lib.csa2_trace_enable.argtypes = [c_int32]
+_lib.csa2_trace_read.restype = c_int
+_lib.csa2_trace_read.argtypes = [POINTER(TraceRecord), c_int32, POINTER(c_int32)]
+_lib.csa2_kernel_name.restype = ctypes.c_char_p
+_lib.csa2_kernel_name.argtypes = [c_int32]
 
 EXPORTED = ("csa2_compress", "csa2_index_topk", "csa2_sparse_attn", "csa2_layer_group", "csa2_workspace_size",
-            "csa2_status_str", "csa2_last_error", "csa2_abi_version")
+            "csa2_status_str", "csa2_last_error", "csa2_abi_version", "csa2_trace_enable", "csa2_trace_read",
+            "csa2_kernel_name")
 
 
 def library() -> ctypes.CDLL:
@@ -165,3 +176,22 @@ def csa2_layer_group(dims, cache, layers, q_pos, n_q, compress, ws, stream=None)
     _check(_lib.csa2_layer_group(ctypes.byref(dims), ctypes.byref(cache), len(layers), arr, ptr(q_pos), n_q,
                                  None if compress is None else ctypes.byref(compress), ptr(ws), ws_bytes,
                                  _stream(stream)))
+
+
+def csa2_trace_enable(max_kernels: int) -> None:
+    """Record device times of up to ``max_kernels`` launches (0 turns tracing off)."""
+    _check(_lib.csa2_trace_enable(max_kernels))
+
+
+def csa2_trace_read(max_records: int = 65536) -> tuple[list[tuple[str, float]], int]:
+    """(kernel name, ms) per recorded launch in launch order, and the dropped count."""
+    buf = (TraceRecord * max_records)()
+    dropped = c_int32(0)
+    n = _lib.csa2_trace_read(buf, max_records, ctypes.byref(dropped))
+    if n < 0:
+        raise Csa2Error(n, "trace read failed")
+    return [(csa2_kernel_name(buf[i].kernel), float(buf[i].ms)) for i in range(n)], int(dropped.value)
+
+
+def csa2_kernel_name(kernel: int) -> str:
+    return _lib.csa2_kernel_name(kernel).decode()

@@ -76,7 +76,9 @@ int check_cache(const csa2_dims* d, const csa2_kv_cache* c, bool need_idx) {
     if (c->idx_group != 16 && c->idx_group != 32) return fail(CSA2_ERR_UNSUPPORTED, "idx_group=%d: need 16 or 32", c->idx_group);
     if (d->d % c->main_group || d->d_idx % c->idx_group) return fail(CSA2_ERR_INVALID_ARG, "widths must be multiples of the FP4 groups");
     if (!c->main_scale) return fail(CSA2_ERR_INVALID_ARG, "FP4 cache needs main_scale");
+    if (!aligned16(c->main_scale)) return fail(CSA2_ERR_INVALID_ARG, "cache main_scale is not 16-byte aligned");
     if (need_idx && !c->idx_scale) return fail(CSA2_ERR_INVALID_ARG, "FP4 cache needs idx_scale");
+    if (c->idx_scale && !aligned16(c->idx_scale)) return fail(CSA2_ERR_INVALID_ARG, "cache idx_scale is not 16-byte aligned");
   }
   return CSA2_OK;
 }

@@ -121,253 +121,410 @@ __global__ __launch_bounds__(kThreads) void attn_generic_kernel(
 
 // ------------------------------------------------------------------ MFMA ---
 //
-// Production shape: d = 512, heads in groups of 32, bf16 queries, bf16 or FP4
-// main KV.  A workgroup (4 waves) owns one (query, head group of 32, run of
-// 32-row tiles); the rows of a query are the kept entries followed by the
-// window rows, padded to whole tiles.  Per tile:
-//   1. the 32 rows are staged in LDS as bf16 (FP4 rows are dequantised on the
-//      way: codes converted exactly, then scaled in float32, exact);
-//   2. logits L^T[row][head] = R . Q^T: wave w contracts its quarter of the
-//      512 channels (8 x v_mfma_f32_32x32x16_bf16) and the four partial sums
-//      are added through LDS;
-//   3. online softmax per head (running max and denominator);
-//   4. O[head][c] += P . R, where P comes straight from the logit registers
-//      (the 32x32 accumulator layout - lane = one column, 16 rows - is the
-//      operand layout of the next product) and R is put in that same layout
-//      by multiplying the staged rows with a 0/1 selection matrix on the
-//      MFMA unit, so no LDS transpose is needed.  Wave w owns channels
-//      [128w, 128w+128) of the output.
-// With several workgroups per (query, head group) each writes its
-// unnormalised partial output and (max, denominator); attn_merge_kernel
-// combines them by log-sum-exp weights.
+// Production shape: d = 512, heads in groups of 16, bf16 queries, bf16 or FP4
+// main KV.  A workgroup (4 waves) owns one (query, group of 16 heads, run of
+// 16-row tiles); the rows of a query are the kept entries followed by the
+// window rows.  Each wave takes every fourth tile and runs it alone - no
+// workgroup barrier inside the loop - double-buffering its tiles in two LDS
+// slabs of its own:
+//   1. a tile's 16 rows are copied global -> LDS with global_load_lds_dwordx4
+//      (one 1 KB row per instruction, lane i -> bytes 16i..16i+15), issued a
+//      tile ahead from inline assembly: the compiler's wait insertion would
+//      drain such copies before every LDS read, so the kernel waits for them
+//      itself.  Every tile issues exactly 16 copies so one wait count covers
+//      it: a row that names no source copies the head group's first query row
+//      (finite data) and is masked out of the softmax.  FP4 rows arrive in
+//      registers (codes and scales, a tile ahead) and are dequantised into
+//      the slab (E2M1 codes converted exactly, times the E4M3 scale in
+//      float32 - exact in bf16);
+//   2. logits L[row][head] = R . Q^T over the 512 channels (16 products of
+//      v_mfma_f32_16x16x32_bf16; rows read from the slab, lane = row; the 16
+//      heads' rotated queries held in registers, lane = head);
+//   3. online softmax per head against a reference max that is raised (with
+//      the output rescaled) only when a logit exceeds it by more than
+//      kRescaleGap; each lane sums only its own rows, reduced once at the end;
+//   4. O^T[channel][head] += R^T . P: the slab is read transposed with
+//      ds_read_b64_tr_b16 (within each 16 lanes,
+//      lane j's element i is element j%4 of the 8 bytes that lane 4i+j/4
+//      addresses), giving lane = channel and 4 consecutive rows - the A
+//      operand of v_mfma_f32_16x16x16_bf16; P is the B operand exactly as the
+//      logits left it, and each lane keeps the head of its softmax state.
+// At the end the four waves' (reference max, sum, O) are combined through LDS
+// in a fixed order.  The head groups of a query are placed on one XCD
+// (workgroups are dealt to the 8 XCDs in turn) so they share the query's rows
+// in that L2.  With several row splits per (query, head group) each workgroup
+// writes its unnormalised output and (reference max, sum); attn_merge_kernel
+// combines them.
 
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
-typedef __bf16 bf16x2_t __attribute__((__vector_size__(4)));
-typedef float f32x16_t __attribute__((__vector_size__(64)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kD = 512;
-constexpr int kRowPitch = kD * 2 + 16;  // bytes per staged row; the pad spreads rows over LDS banks
+constexpr int kPitch = kD * 2 + 32;  // LDS bytes per row: the pad puts the 4 rows of a transposed read on distinct banks
+constexpr int kSlab = 16 * kPitch;   // one 16-row tile
+constexpr int kLdsLoop = 4 * 2 * kSlab;  // two slabs per wave
+constexpr int kLdsSlabs = 4 * 16 * kD * 4;  // the four waves' fp32 outputs at the end, reusing the loop space
+constexpr int kLdsMl = kLdsLoop > kLdsSlabs ? kLdsLoop : kLdsSlabs;  // (max, sum) of the four waves
+constexpr int kLdsRope = kLdsMl + 2 * 4 * 16 * 4;                     // (cos, sin) per rotary pair
+constexpr int kLdsIds = kLdsRope + 2 * 64 * 4;                        // kept-entry ids of the workgroup's rows
+constexpr int kMaxIds = 2048 + 16;                                    // topk <= 2048, plus a straddling tile
+constexpr int kAttnLds = kLdsIds + kMaxIds * 4;
+// Softmax reference: logits are exponentiated against a per-head reference
+// max that is raised (and the output rescaled) only when a logit exceeds it
+// by more than this, so P stays below e^8 and the sums far from overflow.
+constexpr float kRescaleGap = 8.0f;
+
+// Copy 16 bytes per lane from global address `src` to LDS byte address
+// `lds_addr` + 16 * lane (global_load_lds_dwordx4; the LDS base goes in M0).
+// Its completion is tracked only by the caller's s_waitcnt vmcnt.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; naming it tells the compiler it changes
+__device__ __forceinline__ void copy_row_to_lds(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr), "v"(src) : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-// 16 FP4 code bytes (32 values) -> 32 bf16 values times their E4M3 scales
-// (s0 for the first 16 values, s1 for the rest); all products are exact.
-__device__ __forceinline__ void dequant_fp4_32(uint4 codes, float s0, float s1, uint4* out) {
-  const uint32_t w[4] = {codes.x, codes.y, codes.z, codes.w};
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float sc = q < 2 ? s0 : s1;
-    bf16x2_t pr[4] = {__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], 1.0f, 0),
-                      __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], 1.0f, 1),
-                      __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], 1.0f, 2),
-                      __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], 1.0f, 3)};
-    bf16x8_t v;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = static_cast<__bf16>(static_cast<float>(pr[i][0]) * sc);
-      v[2 * i + 1] = static_cast<__bf16>(static_cast<float>(pr[i][1]) * sc);
-    }
-    out[q] = __builtin_bit_cast(uint4, v);
-  }
-}
-
-__device__ __forceinline__ int acc_row(int i, int half) { return 8 * (i >> 2) + 4 * half + (i & 3); }
-
-// Value of v held by lane src (lower half) or src + 4 (upper half): the head
-// of accumulator row acc_row(i, half).  Two uniform readlanes and a select
-// instead of a cross-lane LDS permute.
-__device__ __forceinline__ float lane_value(float v, int src, int half) {
-  const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src));
-  const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src + 4));
-  return half ? hi : lo;
-}
-
+// First channel of k-chunk k (8 channels) held by lane group g in the operands
+// of the logit products.  bf16 caches: chunk k covers channels [32k, 32k+32)
+// so each load instruction reads 64 contiguous bytes per row.  FP4 caches:
+// lane group g covers channels [128g, 128g+128), so its codes are 64
+// contiguous bytes.  The contraction may run in any channel order as long as
+// both operands use the same one.
 template <bool FP4>
-__global__ __launch_bounds__(256) void attn_mfma_kernel(
-    int H, int topk, int window, int main_group, int d_rope, int64_t capacity, RopeTable rope,
-    const uint16_t* __restrict__ q, const int32_t* __restrict__ q_pos, int n_q, const int32_t* __restrict__ topk_ids,
-    const uint16_t* __restrict__ swa, const int32_t* __restrict__ swa_first, int n_swa,
-    const uint8_t* __restrict__ main, const uint8_t* __restrict__ main_scale, int n_tiles, int tiles_per_split,
-    int n_splits, uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
-    float* __restrict__ part_ml) {
-  __shared__ __align__(16) uint8_t rt[32 * kRowPitch];
-  __shared__ float lpart[4][16][64];
-  __shared__ int rvalid[32];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 31, h = lane >> 5;
-  const int split = blockIdx.x, hg = blockIdx.y;
-  const int64_t bq = blockIdx.z, b = bq / n_q;
-  const int64_t t = q_pos[bq];
+__device__ __forceinline__ int chan0(int g, int k) { return FP4 ? 128 * g + 8 * k : 32 * k + 8 * g; }
 
-  // B operand of the logits: the rotated query, lane = head, this wave's channel quarter
-  bf16x8_t qop[8];
-  {
-    const uint16_t* qrow = q + (bq * H + hg * 32 + n) * kD;
-    const int c_rot0 = kD - d_rope;
+// 8 E2M1 codes (one 32-bit word, low nibble first) times scale s -> 8 bf16.
+__device__ __forceinline__ uint4 dequant8(uint32_t w, float s) {
+  const f32x2 f[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0),
+                      __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1),
+                      __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2),
+                      __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3)};
+  bf16x8_t v;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int c0 = 128 * wave + 16 * s + 8 * h;
-      bf16x8_t v = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + c0));
-      if (c0 + 8 > c_rot0) {
-#pragma unroll
-        for (int pi = 0; pi < 4; ++pi) {
-          const int c = c0 + 2 * pi;
-          if (c >= c_rot0) {
-            const double phi = double(t) * rope.inv_freq[(c - c_rot0) / 2];
-            const double two_pi = 6.283185307179586476925, inv_two_pi = 0.15915494309189533577;
-            const float red = float(phi - two_pi * rint(phi * inv_two_pi));  // angle reduced in float64
-            float sn, cs;
-            sincosf(red, &sn, &cs);
-            const float x = static_cast<float>(v[2 * pi]), y = static_cast<float>(v[2 * pi + 1]);
-            v[2 * pi] = static_cast<__bf16>(x * cs - y * sn);
-            v[2 * pi + 1] = static_cast<__bf16>(x * sn + y * cs);
-          }
-        }
-      }
-      qop[s] = v;
-    }
+  for (int p = 0; p < 4; ++p) {
+    v[2 * p] = static_cast<__bf16>(f[p][0] * s);
+    v[2 * p + 1] = static_cast<__bf16>(f[p][1] * s);
   }
-  // 0/1 selection operands that turn staged rows into the P.R operand layout
-  bf16x8_t eop[2];
-#pragma unroll
-  for (int e = 0; e < 2; ++e)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) eop[e][i] = static_cast<__bf16>(n == 16 * e + 8 * h + i ? 1.0f : 0.0f);
+  return __builtin_bit_cast(uint4, v);
+}
 
-  const float scale = 0.044194173824159216f;  // 1/sqrt(512)
-  float m_run = -INFINITY, l_run = 0.0f;
-  f32x16_t oacc[4];
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb) oacc[cb] = f32x16_t{};
-  const int64_t win0 = t - window + 1 > 0 ? t - window + 1 : 0;
-  const int64_t sfirst = swa ? swa_first[b] : 0;
+// FP4 codes of a lane's part of its row (channels 128g .. 128g+127) and the
+// row's scales (all 16 bytes for groups of 32; for groups of 16 the 16 bytes
+// holding this lane's 8).
+struct Fp4Regs {
+  uint4 c[4];
+  uint4 sc;
+};
+
+// Per-tile facts, uniform across the wave: bit i = row i of the tile.
+struct TileMask {
+  uint32_t valid;  // the row has a source
+  uint32_t fp4;    // the row is an FP4 cache row
+};
+
+// FP4: the cache is FP4 with one E4M3 scale per MG channels (MG = 16 or 32).
+template <bool FP4, int MG>
+__global__ __launch_bounds__(256) void attn_mfma_kernel(
+    int H, int topk, int window, int d_rope, int64_t capacity, RopeTable rope,
+    const uint16_t* __restrict__ q, const int32_t* __restrict__ q_pos, int n_q, int64_t n_bq,
+    const int32_t* __restrict__ topk_ids, const uint16_t* __restrict__ swa, const int32_t* __restrict__ swa_first,
+    int n_swa, const uint8_t* __restrict__ main, const uint8_t* __restrict__ main_scale, int n_tiles,
+    int tiles_per_split, int n_splits, uint16_t* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ part_o, float* __restrict__ part_ml) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int G = H / 16, U = n_splits * G;
+  const int64_t wg = blockIdx.x, x8 = wg & 7, rest = wg >> 3;
+  const int u = int(rest % U);
+  const int64_t bq = (rest / U) * 8 + x8;
+  if (bq >= n_bq) return;  // padding workgroup (uniform)
+  const int split = u / G, hg = u % G;
+  const int64_t b = bq / n_q, t = q_pos[bq];
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint8_t* rs = lds + wave * 2 * kSlab;
+
   const int tile_lo = split * tiles_per_split;
   const int tile_hi = min(n_tiles, tile_lo + tiles_per_split);
+  const int64_t win0 = t - window + 1 > 0 ? t - window + 1 : 0;
+  const int64_t sfirst = swa ? swa_first[b] : 0;
+  const uint16_t* qrow0 = q + (bq * H + hg * 16) * kD;  // finite stand-in for rows with no source
 
-  for (int tile = tile_lo; tile < tile_hi; ++tile) {
-    // ---- 1. stage 32 rows (8 threads per row, 16-byte chunks interleaved) ----
-    {
-      const int rr = tid >> 3, p = tid & 7;
-      const int64_t r = int64_t(tile) * 32 + rr;
-      int64_t crow = -1, srow = -1;
-      if (r < topk) {
-        const int64_t j = topk_ids[bq * topk + r];
-        if (j >= 0 && j < capacity) crow = b * capacity + j;
-      } else if (r < topk + window) {
-        const int64_t pp = win0 + (r - topk), sidx = pp - sfirst;
-        if (swa && pp <= t && sidx >= 0 && sidx < n_swa) srow = b * n_swa + sidx;
-      }
-      uint8_t* dst = rt + rr * kRowPitch;
-      if (FP4 && crow >= 0) {
+  // kept-entry ids of this workgroup's rows, and the rotation of this query's
+  // position for each rotary pair, once per workgroup
+  int32_t* ids_lds = reinterpret_cast<int32_t*>(lds + kLdsIds);
+  const int row_lo = tile_lo * 16;
+  {
+    const int r_end = min(tile_hi * 16, topk);
+    int32_t idv[(kMaxIds + 255) / 256];
 #pragma unroll
-        for (int v = 0; v < 2; ++v) {
-          const int ch = p + 8 * v;  // 32-value chunk of the row
-          const uint4 codes = *reinterpret_cast<const uint4*>(main + crow * (kD / 2) + 16 * ch);
-          float s0, s1;
-          if (main_group == 32) {
-            s0 = s1 = e4m3_to_f32(main_scale[crow * (kD / 32) + ch]);
-          } else {
-            s0 = e4m3_to_f32(main_scale[crow * (kD / 16) + 2 * ch]);
-            s1 = e4m3_to_f32(main_scale[crow * (kD / 16) + 2 * ch + 1]);
-          }
-          uint4 o[4];
-          dequant_fp4_32(codes, s0, s1, o);
+    for (int i = 0; i < (kMaxIds + 255) / 256; ++i) {  // all loads first, then the stores
+      const int r = row_lo + tid + 256 * i;
+      idv[i] = r < r_end ? topk_ids[bq * topk + r] : 0;
+    }
 #pragma unroll
-          for (int u = 0; u < 4; ++u) *reinterpret_cast<uint4*>(dst + (4 * ch + u) * 16) = o[u];
+    for (int i = 0; i < (kMaxIds + 255) / 256; ++i) {
+      const int r = row_lo + tid + 256 * i;
+      if (r < r_end) ids_lds[r - row_lo] = idv[i];
+    }
+  }
+  float* rtab = reinterpret_cast<float*>(lds + kLdsRope);
+  if (tid < d_rope / 2) {
+    const double phi = double(t) * rope.inv_freq[tid];
+    const double two_pi = 6.283185307179586476925, inv_two_pi = 0.15915494309189533577;
+    const float red = float(phi - two_pi * rint(phi * inv_two_pi));  // angle reduced in float64
+    float sn, cs;
+    sincosf(red, &sn, &cs);
+    rtab[2 * tid] = cs;
+    rtab[2 * tid + 1] = sn;
+  }
+  // B operand of the logits: head l16's query, chunk k = channels chan0(g, k) .. +8
+  bf16x8_t qtmp[16];
+  {
+    const uint16_t* qrow = qrow0 + l16 * kD;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) qtmp[k] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + chan0<FP4>(g, k)));
+  }
+  // Complete every load so far with a wait the compiler sees: its own waits
+  // count only the loads it knows of, and inside the loop the row copies it
+  // does not know of would make any vmcnt it inserts drain them too.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  {
+    const int c_rot0 = kD - d_rope;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if (!FP4 && 32 * k + 32 <= c_rot0) continue;  // no rotary channel in this chunk (uniform)
+#pragma unroll
+      for (int pi = 0; pi < 4; ++pi) {
+        const int c = chan0<FP4>(g, k) + 2 * pi;
+        const int m = c >= c_rot0 ? (c - c_rot0) / 2 : 0;
+        const float cs = rtab[2 * m], sn = rtab[2 * m + 1];
+        const float x = static_cast<float>(qtmp[k][2 * pi]), y = static_cast<float>(qtmp[k][2 * pi + 1]);
+        if (c >= c_rot0) {
+          qtmp[k][2 * pi] = static_cast<__bf16>(x * cs - y * sn);
+          qtmp[k][2 * pi + 1] = static_cast<__bf16>(x * sn + y * cs);
         }
-      } else if (crow >= 0 || srow >= 0) {
-        const uint4* src = crow >= 0 ? reinterpret_cast<const uint4*>(main + crow * (kD * 2))
-                                     : reinterpret_cast<const uint4*>(swa + srow * kD);
-#pragma unroll
-        for (int v = 0; v < 8; ++v) *reinterpret_cast<uint4*>(dst + (p + 8 * v) * 16) = src[p + 8 * v];
-      } else {
-#pragma unroll
-        for (int v = 0; v < 8; ++v) *reinterpret_cast<uint4*>(dst + (p + 8 * v) * 16) = make_uint4(0, 0, 0, 0);
       }
-      if (p == 0) rvalid[rr] = (crow >= 0 || srow >= 0);
     }
-    __syncthreads();
+  }
+  const bf16x8_t* qreg = qtmp;
 
-    // ---- 2. logits over this wave's channel quarter, summed across waves ----
-    bf16x8_t aop[8];
-    f32x16_t lacc = f32x16_t{};
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int c0 = 128 * wave + 16 * s + 8 * h;
-      aop[s] = *reinterpret_cast<const bf16x8_t*>(rt + n * kRowPitch + c0 * 2);
-      lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[s], qop[s], lacc, 0, 0, 0);
+  // Issue the copies of `tile` into slab `buf`: for FP4 caches this lane's
+  // codes and scales into `fr` first (5 loads), then the 16 row copies.
+  // Returns uniform row masks.
+  auto issue = [&](int tile, int buf, Fp4Regs& fr) -> TileMask {
+    // lanes 0..15 (and their copies in the other lane groups) work out rows 0..15
+    const int64_t r = int64_t(tile) * 16 + l16;
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(qrow0);
+    int64_t crow = 0;
+    bool valid = false, fp4 = false;
+    if (r < topk) {
+      const int64_t j = ids_lds[r - row_lo];
+      if (j >= 0 && j < capacity) {
+        valid = true;
+        crow = b * capacity + j;
+        if (FP4) fp4 = true;
+        else src = main + crow * (kD * 2);
+      }
+    } else if (r < topk + window) {
+      const int64_t pp = win0 + (r - topk), sidx = pp - sfirst;
+      if (swa && pp <= t && sidx >= 0 && sidx < n_swa) {
+        valid = true;
+        src = reinterpret_cast<const uint8_t*>(swa + (b * n_swa + sidx) * kD);
+      }
     }
+    TileMask m;
+    m.valid = uint32_t(__ballot(valid)) & 0xFFFFu;  // lanes 0..15 hold rows 0..15
+    m.fp4 = uint32_t(__ballot(fp4)) & 0xFFFFu;
+    if constexpr (FP4) {
+      const uint8_t* codes = main + crow * (kD / 2) + 64 * g;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) lpart[wave][i][lane] = lacc[i];
-    __syncthreads();
-    float lg[16];
-    float tmax = -INFINITY;
+      for (int i = 0; i < 4; ++i) fr.c[i] = reinterpret_cast<const uint4*>(codes)[i];
+      fr.sc = *reinterpret_cast<const uint4*>(main_scale + crow * (kD / MG) + (MG == 16 ? 16 * (g >> 1) : 0));
+    }
+    const uint32_t slab = __builtin_amdgcn_readfirstlane(
+        uint32_t(reinterpret_cast<uintptr_t>((lds_void*)(rs + buf * kSlab))));
+    const uint64_t src_u = reinterpret_cast<uint64_t>(src);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float v = (lpart[0][i][lane] + lpart[1][i][lane] + lpart[2][i][lane] + lpart[3][i][lane]) * scale;
-      lg[i] = rvalid[acc_row(i, h)] ? v : -INFINITY;
-      tmax = fmaxf(tmax, lg[i]);
+      const uint64_t row = (uint64_t(uint32_t(__builtin_amdgcn_readlane(int(src_u >> 32), i))) << 32) |
+                           uint32_t(__builtin_amdgcn_readlane(int(uint32_t(src_u)), i));
+      copy_row_to_lds(reinterpret_cast<const void*>(row + 16 * lane), slab + i * kPitch);
+    }
+    return m;
+  };
+
+  const float scale = 0.044194173824159216f;  // 1/sqrt(512)
+  float m_ref = -INFINITY, l_part = 0.0f;  // l_part: this lane's rows only
+  f32x4 oacc[32];
+#pragma unroll
+  for (int cb = 0; cb < 32; ++cb) oacc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // FP4 rows of a tile into its slab, from `fr`: waits for everything issued
+  // so far (this tile's loads are the youngest).
+  auto dequant_tile = [&](int buf, const TileMask m, const Fp4Regs& fr) {
+    uint8_t* slab = rs + buf * kSlab;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if ((m.fp4 >> l16) & 1u) {
+      const uint32_t w4[16] = {fr.c[0].x, fr.c[0].y, fr.c[0].z, fr.c[0].w, fr.c[1].x, fr.c[1].y,
+                               fr.c[1].z, fr.c[1].w, fr.c[2].x, fr.c[2].y, fr.c[2].z, fr.c[2].w,
+                               fr.c[3].x, fr.c[3].y, fr.c[3].z, fr.c[3].w};
+      // this lane's scales: scales 4g .. 4g+3 of the row (groups of 32), or
+      // 8g .. 8g+7 (groups of 16: bytes 8(g&1) .. of the 16 loaded)
+      const uint32_t scw[4] = {fr.sc.x, fr.sc.y, fr.sc.z, fr.sc.w};
+      uint32_t sw[2];
+      if constexpr (MG == 32) {
+        sw[0] = scw[g];
+        sw[1] = 0u;
+      } else {
+        sw[0] = scw[2 * (g & 1)];
+        sw[1] = scw[2 * (g & 1) + 1];
+      }
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        // channels 128g + 8k: scale (8k)/MG among this lane's 128/MG
+        const int si = (8 * k) / MG;
+        *reinterpret_cast<uint4*>(slab + l16 * kPitch + (128 * g + 8 * k) * 2) =
+            dequant8(w4[k], e4m3_to_f32((sw[si >> 2] >> (8 * (si & 3))) & 0xFFu));
+      }
+    }
+  };
+
+  // Compute the tile in slab `buf`.  `more`: the next tile's 16 copies were
+  // issued after this tile's and may stay in flight (bf16 caches; for FP4 the
+  // wait happened in dequant_tile).
+  auto compute = [&](int buf, const TileMask m, bool more) {
+    const uint8_t* slab = rs + buf * kSlab;
+    if constexpr (!FP4) {
+      if (more) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    // ---- logits: lane holds head l16, rows 4g + r of the tile ----
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(slab + l16 * kPitch + chan0<FP4>(g, k) * 2);
+      const bf16x8_t qb = qreg[k];
+      if (k & 1) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb, acc1, 0, 0, 0);
+      else acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb, acc0, 0, 0, 0);
     }
 
-    // ---- 3. online softmax for head n (rows split between lanes n and n+32) ----
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = m_new == -INFINITY ? 1.0f : __expf(m_run - m_new);
-    float psum = 0.0f;
-    bf16x8_t pop[2];
+    // ---- online softmax for head l16: reference max m_ref, per-lane partial sums ----
+    float lg[4], mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float pv = lg[i] == -INFINITY ? 0.0f : __expf(lg[i] - m_new);
-      psum += pv;
-      pop[i >> 3][i & 7] = static_cast<__bf16>(pv);
+    for (int r = 0; r < 4; ++r) {
+      lg[r] = ((m.valid >> (4 * g + r)) & 1u) ? (acc0[r] + acc1[r]) * scale : -INFINITY;
+      mx = fmaxf(mx, lg[r]);
     }
-    psum += __shfl_xor(psum, 32, kWave);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    if (__ballot(mx > m_ref + kRescaleGap)) {  // rare: raise the reference to the head's max
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const float m_new = fmaxf(m_ref, mx);
+      if (m_ref != -INFINITY && __ballot(m_new != m_ref)) {
+        const float alpha = __expf(m_ref - m_new);
+        l_part *= alpha;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float a = lane_value(alpha, acc_row(i, 0), h);
+        for (int cb = 0; cb < 32; ++cb) oacc[cb] *= alpha;
+      }
+      m_ref = m_new;
+    }
+    s16x4 pop;
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) oacc[cb][i] *= a;
+    for (int r = 0; r < 4; ++r) {
+      const float p = lg[r] == -INFINITY ? 0.0f : __expf(lg[r] - m_ref);
+      l_part += p;
+      pop[r] = __builtin_bit_cast(short, static_cast<__bf16>(p));
     }
 
-    // ---- 4. rows into operand layout, then O += P . R for this wave's channels ----
+    // ---- O^T += R^T . P, rows read transposed from the slab ----
+    const uint8_t* tr_base = slab + (4 * g + (l16 >> 2)) * kPitch + 4 * (l16 & 3) * 2;
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      f32x16_t ct = f32x16_t{};
-      ct = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[2 * cb], eop[0], ct, 0, 0, 0);
-      ct = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[2 * cb + 1], eop[1], ct, 0, 0, 0);
-      bf16x8_t rop[2];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) rop[i >> 3][i & 7] = static_cast<__bf16>(ct[i]);
-      oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pop[0], rop[0], oacc[cb], 0, 0, 0);
-      oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pop[1], rop[1], oacc[cb], 0, 0, 0);
+    for (int cb = 0; cb < 32; ++cb) {
+      const s16x4 at = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tr_base + 32 * cb));
+      oacc[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(at, pop, oacc[cb], 0, 0, 0);
     }
-    __syncthreads();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slab reads done before it is refilled
+  };
+
+  Fp4Regs fa{}, fb{};
+  int tile = tile_lo + wave;
+  TileMask ma{0u, 0u}, mb{0u, 0u};
+  if (tile < tile_hi) ma = issue(tile, 0, fa);
+  while (tile < tile_hi) {
+    const bool more_a = tile + 4 < tile_hi;
+    if constexpr (FP4) dequant_tile(0, ma, fa);
+    if (more_a) mb = issue(tile + 4, 1, fb);
+    compute(0, ma, more_a);
+    tile += 4;
+    if (tile >= tile_hi) break;
+    const bool more_b = tile + 4 < tile_hi;
+    if constexpr (FP4) dequant_tile(1, mb, fb);
+    if (more_b) ma = issue(tile + 4, 0, fa);
+    compute(1, mb, more_b);
+    tile += 4;
   }
 
-  // ---- outputs: lane holds channel 128w + 32cb + n of heads acc_row(i, h) ----
+  // ---- combine the four waves (fixed order), then store ----
+  __syncthreads();  // every wave is done with its slabs
+  float* slabs = reinterpret_cast<float*>(lds);
+  float* mls = reinterpret_cast<float*>(lds + kLdsMl);
+  l_part += __shfl_xor(l_part, 16, kWave);
+  l_part += __shfl_xor(l_part, 32, kWave);
+  if (g == 0) {
+    mls[wave * 16 + l16] = m_ref;
+    mls[64 + wave * 16 + l16] = l_part;
+  }
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) M = fmaxf(M, mls[w * 16 + l16]);
+  float L = 0.0f, f_own = 0.0f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float mw = mls[w * 16 + l16];
+    const float f = mw == -INFINITY ? 0.0f : __expf(mw - M);
+    L += f * mls[64 + w * 16 + l16];
+    if (w == wave) f_own = f;
+  }
+  float* my = slabs + wave * (16 * kD);
+#pragma unroll
+  for (int cb = 0; cb < 32; ++cb) *reinterpret_cast<f32x4*>(my + (cb * 64 + lane) * 4) = oacc[cb] * f_own;
+  __syncthreads();
+  const int64_t head = int64_t(hg) * 16 + l16;
   if (n_splits == 1) {
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int hh = acc_row(i, h);
-      const float lh = lane_value(l_run, acc_row(i, 0), h);
-      const float inv = lh > 0.0f ? 1.0f / lh : 0.0f;
-      uint16_t* orow = out + (bq * H + hg * 32 + hh) * kD + 128 * wave + n;
+    for (int i = 0; i < 8; ++i) {
+      const int cb = wave * 8 + i;
+      f32x4 s = *reinterpret_cast<const f32x4*>(slabs + (cb * 64 + lane) * 4);
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) orow[32 * cb] = f32_to_bf16(oacc[cb][i] * inv);
+      for (int w = 1; w < 4; ++w) s += *reinterpret_cast<const f32x4*>(slabs + w * (16 * kD) + (cb * 64 + lane) * 4);
+      uint2 pk;
+      pk.x = uint32_t(f32_to_bf16(s[0] * inv)) | (uint32_t(f32_to_bf16(s[1] * inv)) << 16);
+      pk.y = uint32_t(f32_to_bf16(s[2] * inv)) | (uint32_t(f32_to_bf16(s[3] * inv)) << 16);
+      *reinterpret_cast<uint2*>(out + (bq * H + head) * kD + 16 * cb + 4 * g) = pk;
     }
-    if (lse && wave == 0 && h == 0) lse[bq * H + hg * 32 + n] = l_run > 0.0f ? m_run + logf(l_run) : -INFINITY;
+    if (lse && wave == 0 && g == 0) lse[bq * H + head] = L > 0.0f ? M + logf(L) : -INFINITY;
   } else {
-    const int64_t prow = (bq * n_splits + split) * H + hg * 32;
+    const int64_t prow = (bq * n_splits + split) * H + head;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float* orow = part_o + (prow + acc_row(i, h)) * kD + 128 * wave + n;
+    for (int i = 0; i < 8; ++i) {
+      const int cb = wave * 8 + i;
+      f32x4 s = *reinterpret_cast<const f32x4*>(slabs + (cb * 64 + lane) * 4);
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) orow[32 * cb] = oacc[cb][i];
+      for (int w = 1; w < 4; ++w) s += *reinterpret_cast<const f32x4*>(slabs + w * (16 * kD) + (cb * 64 + lane) * 4);
+      *reinterpret_cast<f32x4*>(part_o + prow * kD + 16 * cb + 4 * g) = s;
     }
-    if (wave == 0 && h == 0) {
-      part_ml[(prow + n) * 2] = m_run;
-      part_ml[(prow + n) * 2 + 1] = l_run;
+    if (wave == 0 && g == 0) {
+      part_ml[prow * 2] = M;
+      part_ml[prow * 2 + 1] = L;
     }
   }
 }
@@ -416,22 +573,29 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(int H, int n_splits, co
 struct AttnPlan {
   bool mfma;
   int n_tiles, tiles_per_split, n_splits;
+  int64_t n_blocks;  // 1-D grid of the MFMA kernel
 };
 
+// Row splits per (query, head group): one while the (query, head group)
+// workgroups alone fill the 256 compute units, otherwise enough to reach
+// about 256 workgroups (each wave's tile stream is latency-bound, so more
+// workgroups in flight beat the cost of merging the splits).
 AttnPlan plan_attn(const csa2_dims& dims, const csa2_kv_cache& cache, int32_t n_q) {
   AttnPlan p{};
-  p.mfma = dims.d == kD && dims.n_heads % 32 == 0 && dims.act_dtype == CSA2_BF16 &&
+  p.mfma = dims.d == kD && dims.n_heads % 16 == 0 && dims.act_dtype == CSA2_BF16 &&
            (cache.kv_dtype == CSA2_BF16 || cache.kv_dtype == CSA2_FP4);
-  p.n_tiles = (dims.topk + dims.window + 31) / 32;
+  p.n_tiles = (dims.topk + dims.window + 15) / 16;
   p.tiles_per_split = p.n_tiles;
   p.n_splits = 1;
   if (!p.mfma || n_q <= 0) return p;
-  const int64_t units = int64_t(cache.batch) * n_q * (dims.n_heads / 32);
-  int splits = int(units >= 512 ? 1 : (512 + units - 1) / units);
+  const int64_t n_bq = int64_t(cache.batch) * n_q, G = dims.n_heads / 16;
+  const int64_t units = n_bq * G;
+  int splits = int(units >= 256 ? 1 : (256 + units - 1) / units);
   splits = splits < 1 ? 1 : (splits > p.n_tiles ? p.n_tiles : splits);
   splits = splits > kMaxSplits ? kMaxSplits : splits;
   p.tiles_per_split = (p.n_tiles + splits - 1) / splits;
   p.n_splits = (p.n_tiles + p.tiles_per_split - 1) / p.tiles_per_split;
+  p.n_blocks = 8 * int64_t(p.n_splits) * G * ((n_bq + 7) / 8);
   return p;
 }
 
@@ -457,26 +621,39 @@ hipError_t launch_attn(const csa2_dims& dims, const csa2_kv_cache& cache, const 
       part_o = static_cast<float*>(ws);
       part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + (rows * kD * 4 + 255) / 256 * 256);
     }
-    const dim3 grid(p.n_splits, dims.n_heads / 32, unsigned(int64_t(cache.batch) * n_q));
-    auto kern = cache.kv_dtype == CSA2_FP4 ? attn_mfma_kernel<true> : attn_mfma_kernel<false>;
-    hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, dims.n_heads, dims.topk, dims.window, cache.main_group,
-                       dims.d_rope, cache.capacity, make_rope_table(dims), static_cast<const uint16_t*>(q), q_pos, n_q, topk,
-                       static_cast<const uint16_t*>(swa_kv), swa_first_pos, n_swa,
-                       static_cast<const uint8_t*>(cache.main), cache.main_scale, p.n_tiles, p.tiles_per_split,
-                       p.n_splits, static_cast<uint16_t*>(out), lse, part_o, part_ml);
-    hipError_t e = hipGetLastError();
+    if (p.n_blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    static bool attr_set = false;
+    if (!attr_set) {
+      for (const void* f : {reinterpret_cast<const void*>(attn_mfma_kernel<false, 32>),
+                            reinterpret_cast<const void*>(attn_mfma_kernel<true, 32>),
+                            reinterpret_cast<const void*>(attn_mfma_kernel<true, 16>)}) {
+        const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kAttnLds);
+        if (e != hipSuccess) return e;
+      }
+      attr_set = true;
+    }
+    auto kern = cache.kv_dtype != CSA2_FP4 ? attn_mfma_kernel<false, 32>
+                : (cache.main_group == 32 ? attn_mfma_kernel<true, 32> : attn_mfma_kernel<true, 16>);
+    hipError_t e = launch_kernel(cache.kv_dtype == CSA2_FP4 ? CSA2_KERNEL_ATTN_FP4 : CSA2_KERNEL_ATTN_BF16, kern,
+                                 dim3(unsigned(p.n_blocks)), dim3(256), kAttnLds, stream, dims.n_heads, dims.topk,
+                                 dims.window, dims.d_rope, cache.capacity, make_rope_table(dims),
+                                 static_cast<const uint16_t*>(q), q_pos, n_q, int64_t(cache.batch) * n_q, topk,
+                                 static_cast<const uint16_t*>(swa_kv), swa_first_pos, n_swa,
+                                 static_cast<const uint8_t*>(cache.main), cache.main_scale, p.n_tiles,
+                                 p.tiles_per_split, p.n_splits, static_cast<uint16_t*>(out), lse, part_o, part_ml);
     if (e != hipSuccess || p.n_splits == 1) return e;
-    hipLaunchKernelGGL(attn_merge_kernel, dim3(dims.n_heads, unsigned(int64_t(cache.batch) * n_q)), dim3(128), 0,
-                       stream, dims.n_heads, p.n_splits, part_o, part_ml, static_cast<uint16_t*>(out), lse);
-    return hipGetLastError();
+    const hipError_t err = launch_kernel(CSA2_KERNEL_ATTN_MERGE, attn_merge_kernel,
+                                         dim3(dims.n_heads, unsigned(int64_t(cache.batch) * n_q)), dim3(128), 0,
+                                         stream, dims.n_heads, p.n_splits, part_o, part_ml, static_cast<uint16_t*>(out), lse);
+    return err;
   }
   const dim3 grid(dims.n_heads, n_q, cache.batch);
   const size_t lds = sizeof(float) * size_t(dims.d + dims.topk + dims.window + kThreads / 64 + 2);
-  hipLaunchKernelGGL(attn_generic_kernel, grid, dim3(kThreads), lds, stream, dims.d, dims.d_rope, dims.n_heads,
+  const hipError_t err = launch_kernel(CSA2_KERNEL_ATTN_GENERIC, attn_generic_kernel, grid, dim3(kThreads), lds, stream, dims.d, dims.d_rope, dims.n_heads,
                      dims.topk, dims.window, int(dims.act_dtype == CSA2_BF16), cache.kv_dtype, cache.main_group,
                      make_rope_table(dims), cache.capacity, q, q_pos, n_q, topk, swa_kv, swa_first_pos, n_swa, cache.main,
                      cache.main_scale, out, lse);
-  return hipGetLastError();
+  return err;
 }
 
 }  // namespace csa2

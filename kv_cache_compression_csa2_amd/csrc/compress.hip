@@ -173,10 +173,10 @@ hipError_t launch_compress(const csa2_dims& dims, const csa2_kv_cache& cache, co
   const int parts = kThreads / (dims.d_idx / 2) > 0 ? kThreads / (dims.d_idx / 2) : 1;
   const size_t lds = sizeof(double) * size_t(dims.d + dims.d_idx + parts * dims.d_idx);
   auto kern = dims.act_dtype == CSA2_BF16 ? compress_kernel<true> : compress_kernel<false>;
-  hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, stream, dims.d, dims.d_rope, dims.d_idx, cache.kv_dtype, cache.main_group, cache.idx_group, cache.ratio,
+  const hipError_t err = launch_kernel(CSA2_KERNEL_COMPRESS, kern, grid, dim3(kThreads), lds, stream, dims.d, dims.d_rope, dims.d_idx, cache.kv_dtype, cache.main_group, cache.idx_group, cache.ratio,
                      cache.capacity, make_rope_table(dims), latent, first_pos, n_pos, pair_logits, w_ik, cache.main,
                      cache.main_scale, cache.idx_k, cache.idx_scale);
-  return hipGetLastError();
+  return err;
 }
 
 }  // namespace csa2

@@ -266,19 +266,19 @@ hipError_t launch_scan(const csa2_dims& dims, const csa2_kv_cache& cache, const 
     const int64_t nsb = ss.dom_cap / 64;
     const dim3 grid(unsigned((nsb + 4 * kSbPerWave - 1) / (4 * kSbPerWave)), n_q, cache.batch);
     auto kern = cache.kv_dtype == CSA2_FP4 ? scan_mfma_fp4_kernel : scan_mfma_bf16_kernel;
-    hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, cache.ratio, cache.capacity,
+    const hipError_t err = launch_kernel(cache.kv_dtype == CSA2_FP4 ? CSA2_KERNEL_SCAN_FP4 : CSA2_KERNEL_SCAN_BF16, kern, grid, dim3(256), 0, stream, cache.ratio, cache.capacity,
                        static_cast<const uint16_t*>(idx_q), head_w, q_pos, n_q, pool_in, dims.cand_blocks,
                        static_cast<const uint8_t*>(cache.idx_k), cache.idx_scale, cache.n_entries, ss.scores, ss.bmax,
                        ss.sbmax, ss.dom_cap);
-    return hipGetLastError();
+    return err;
   }
   const dim3 grid(unsigned(ss.dom_cap / kThreads), n_q, cache.batch);
   const size_t lds = sizeof(float) * size_t(dims.n_idx_heads * dims.d_idx + dims.n_idx_heads + kThreads);
-  hipLaunchKernelGGL(scan_generic_kernel, grid, dim3(kThreads), lds, stream, dims.n_idx_heads, dims.d_idx,
+  const hipError_t err = launch_kernel(CSA2_KERNEL_SCAN_GENERIC, scan_generic_kernel, grid, dim3(kThreads), lds, stream, dims.n_idx_heads, dims.d_idx,
                      int(dims.act_dtype == CSA2_BF16), cache.kv_dtype, cache.idx_group, cache.ratio, cache.capacity,
                      idx_q, head_w, q_pos, n_q, pool_in, dims.cand_blocks, cache.idx_k, cache.idx_scale,
                      cache.n_entries, ss.scores, ss.bmax, ss.sbmax, ss.dom_cap);
-  return hipGetLastError();
+  return err;
 }
 
 }  // namespace csa2

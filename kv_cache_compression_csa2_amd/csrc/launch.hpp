@@ -3,6 +3,7 @@
 // the hipError_t of its launches.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -48,6 +49,33 @@ hipError_t launch_select(const csa2_dims& dims, const csa2_kv_cache& cache, cons
 hipError_t launch_attn(const csa2_dims& dims, const csa2_kv_cache& cache, const void* q, const int32_t* q_pos,
                        int32_t n_q, const int32_t* topk, const void* swa_kv, const int32_t* swa_first_pos,
                        int32_t n_swa, void* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+
+// Kernel trace hooks (trace.cpp).  trace_begin hands out a slot with two
+// events for the next launch (slot -1 and no events when tracing is off);
+// trace_end marks whether that launch was enqueued.
+struct TraceSlot {
+  int slot;
+  hipEvent_t start, stop;
+};
+TraceSlot trace_begin(int32_t kernel);
+void trace_end(int slot, bool launched);
+
+// Launch `kern` on `stream` and return the launch's error.  With the kernel
+// trace on, the launch carries the slot's events, which the runtime stamps
+// with the kernel's own start and end times (no extra queue packets).
+template <typename K, typename... Args>
+hipError_t launch_kernel(int32_t kernel_id, K kern, dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                         Args... args) {
+  const TraceSlot t = trace_begin(kernel_id);
+  if (t.slot < 0) {
+    hipLaunchKernelGGL(kern, grid, block, lds, stream, args...);
+    return hipGetLastError();
+  }
+  hipExtLaunchKernelGGL(kern, grid, block, uint32_t(lds), stream, t.start, t.stop, 0u, args...);
+  const hipError_t e = hipGetLastError();
+  trace_end(t.slot, e == hipSuccess);
+  return e;
+}
 
 size_t attn_workspace_bytes(const csa2_dims& dims, const csa2_kv_cache& cache, int32_t n_q);
 

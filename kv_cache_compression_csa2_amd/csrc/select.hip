@@ -202,6 +202,31 @@ __device__ __forceinline__ uint32_t key_in(const float* a, int64_t i, int64_t n)
   return (i >= 0 && i < n) ? score_key(a[i]) : kKeyNegInf;
 }
 
+// keys[p] = key of src[idx(p)] for p in [0, cnt): kKeyForced where idx(p) is
+// `forced`, kKeyNegInf where idx(p) lies outside [0, n).  Each thread issues
+// kPer loads (at clamped, always valid addresses) before it uses any, so the
+// latencies of a batch overlap instead of adding up.  n >= 1.
+template <class IdxFn>
+__device__ __forceinline__ void gather_keys(lds_u32* keys, int cnt, const float* __restrict__ src, int n,
+                                            int forced, IdxFn idx) {
+  constexpr int kPer = 8;
+  for (int base = 0; base < cnt; base += kPer * kNT) {
+    int id[kPer];
+    float v[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int p = base + i * kNT + int(threadIdx.x);
+      id[i] = p < cnt ? idx(p) : -1;
+      v[i] = src[min(max(id[i], 0), n - 1)];
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int p = base + i * kNT + int(threadIdx.x);
+      if (p < cnt) keys[p] = id[i] == forced ? kKeyForced : ((id[i] >= 0 && id[i] < n) ? score_key(v[i]) : kKeyNegInf);
+    }
+  }
+}
+
 __global__ __launch_bounds__(kNT) void select_kernel(int topk, int cand_blocks, int ratio, int64_t capacity,
                                                      const int32_t* __restrict__ q_pos, int n_q,
                                                      const int32_t* __restrict__ pool_in,
@@ -224,57 +249,79 @@ __global__ __launch_bounds__(kNT) void select_kernel(int topk, int cand_blocks, 
   const int qi = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int64_t row = int64_t(b) * n_q + qi;
   const int nsb = int(dom_cap / 64);
-  const int64_t nb = dom_cap / 8;
+  const int nb = int(dom_cap / 8);
   const float* sc = scores + row * dom_cap;
   const float* bm = bmax + row * nb;
   const float* sbm = sbmax + row * nsb;
 
   // ---- HSI pool (full domain only) ----
+  // nbsel blocks chosen for the top-k stage, their ids in lb[0 .. nbsel)
+  int nbsel = -1;
   if (pool_out) {
     const int64_t n = clamp_entries(n_entries, b, capacity);
     const int64_t n_vis = visible_count(n, q_pos[row], ratio);
-    const int64_t fb = n_vis > 0 ? (n_vis - 1) / 8 : -1;
-    const int64_t fsb = fb >= 0 ? fb / 8 : -1;
+    const int fb = n_vis > 0 ? int((n_vis - 1) / 8) : -1;
+    const int fsb = fb >= 0 ? fb / 8 : -1;
     int na = nsb;
     if (nsb > cand_blocks) {
-      for (int p = tid; p < nsb; p += kNT) L.keys[p] = p == fsb ? kKeyForced : key_in(sbm, p, nsb);
+      gather_keys(L.keys, nsb, sbm, nsb, fsb, [](int p) { return p; });
       __syncthreads();
       na = select_top(L, nsb, cand_blocks, L.la);
     } else {
       for (int p = tid; p < nsb; p += kNT) L.la[p] = uint32_t(p);
       __syncthreads();  // la is read across threads below
     }
-    for (int p = tid; p < 8 * na; p += kNT) {
-      const int64_t blk = int64_t(L.la[p >> 3]) * 8 + (p & 7);
-      L.keys[p] = blk == fb ? kKeyForced : key_in(bm, blk, nb);
-    }
+    gather_keys(L.keys, 8 * na, bm, nb, fb, [&](int p) { return int(L.la[p >> 3]) * 8 + (p & 7); });
     __syncthreads();
-    const int nbsel = select_top(L, 8 * na, cand_blocks, L.lb);
-    for (int x = tid; x < cand_blocks; x += kNT) {
-      int32_t v = -1;
-      if (x < nbsel) v = int32_t(min(int64_t(L.la[L.lb[x] >> 3]) * 8 + (L.lb[x] & 7), nb - 1));
-      pool_out[row * cand_blocks + x] = v;
+    const int npool = select_top(L, 8 * na, cand_blocks, L.lb);
+    // pool block ids (ascending), in place: thread x reads and writes lb[x] only
+    for (int x = tid; x < npool; x += kNT) L.lb[x] = min(L.la[L.lb[x] >> 3] * 8 + (L.lb[x] & 7), uint32_t(nb - 1));
+    for (int x = tid; x < cand_blocks; x += kNT) pool_out[row * cand_blocks + x] = x < npool ? int32_t(L.lb[x]) : -1;
+    __syncthreads();
+    // The best topk blocks by their own maxima all lie in the pool when
+    // topk <= cand_blocks - 1: the pool holds the best cand_blocks - 1 blocks
+    // other than the forced one.  So the top-k stage needs only the pool.
+    if (topk < cand_blocks) {
+      gather_keys(L.keys, npool, bm, nb, -1, [&](int p) { return int(L.lb[p]); });
+      __syncthreads();
+      nbsel = select_top(L, npool, topk, L.la);
+      uint32_t ids[kMaxList / kNT];
+#pragma unroll
+      for (int i = 0; i < kMaxList / kNT; ++i) {
+        const int x = tid + i * kNT;
+        ids[i] = x < nbsel ? L.lb[L.la[x]] : 0u;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < kMaxList / kNT; ++i) {
+        const int x = tid + i * kNT;
+        if (x < nbsel) L.lb[x] = ids[i];
+      }
+      __syncthreads();
     }
+  }
+
+  // ---- top-k blocks over the whole domain (unless the pool gave them) ----
+  if (nbsel < 0) {
+    int na = nsb;
+    if (nsb > topk) {
+      gather_keys(L.keys, nsb, sbm, nsb, -1, [](int p) { return p; });
+      __syncthreads();
+      na = select_top(L, nsb, topk, L.la);
+    } else {
+      for (int p = tid; p < nsb; p += kNT) L.la[p] = uint32_t(p);
+      __syncthreads();  // la is read across threads below
+    }
+    gather_keys(L.keys, 8 * na, bm, nb, -1, [&](int p) { return int(L.la[p >> 3]) * 8 + (p & 7); });
+    __syncthreads();
+    nbsel = select_top(L, 8 * na, topk, L.lb);
+    // block ids of the chosen blocks (ascending), in place
+    for (int x = tid; x < nbsel; x += kNT) L.lb[x] = L.la[L.lb[x] >> 3] * 8 + (L.lb[x] & 7);
     __syncthreads();
   }
 
-  // ---- top-k entries ----
-  int na = nsb;
-  if (nsb > topk) {
-    for (int p = tid; p < nsb; p += kNT) L.keys[p] = key_in(sbm, p, nsb);
-    __syncthreads();
-    na = select_top(L, nsb, topk, L.la);
-  } else {
-    for (int p = tid; p < nsb; p += kNT) L.la[p] = uint32_t(p);
-    __syncthreads();  // la is read across threads below
-  }
-  for (int p = tid; p < 8 * na; p += kNT) L.keys[p] = key_in(bm, int64_t(L.la[p >> 3]) * 8 + (p & 7), nb);
-  __syncthreads();
-  const int nbsel = select_top(L, 8 * na, topk, L.lb);
-  // block ids of the chosen blocks (ascending)
-  for (int x = tid; x < nbsel; x += kNT) L.lb[x] = L.la[L.lb[x] >> 3] * 8 + (L.lb[x] & 7);
-  __syncthreads();
-  for (int p = tid; p < 8 * nbsel; p += kNT) L.keys[p] = key_in(sc, int64_t(L.lb[p >> 3]) * 8 + (p & 7), dom_cap);
+  // ---- top-k entries inside the chosen blocks ----
+  gather_keys(L.keys, 8 * nbsel, sc, int(dom_cap), -1, [&](int p) { return int(L.lb[p >> 3]) * 8 + (p & 7); });
   __syncthreads();
   const int ne = select_top(L, 8 * nbsel, topk, L.la);
   for (int x = tid; x < topk; x += kNT) {
@@ -305,10 +352,10 @@ hipError_t launch_select(const csa2_dims& dims, const csa2_kv_cache& cache, cons
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(select_kernel, dim3(n_q, cache.batch), dim3(kNT), kSelectLds, stream, dims.topk,
+  const hipError_t err = launch_kernel(CSA2_KERNEL_SELECT, select_kernel, dim3(n_q, cache.batch), dim3(kNT), kSelectLds, stream, dims.topk,
                      dims.cand_blocks, cache.ratio, cache.capacity, q_pos, n_q, pool_in, cache.n_entries, ss.scores,
                      ss.bmax, ss.sbmax, ss.dom_cap, topk_out, pool_out, topk_scores);
-  return hipGetLastError();
+  return err;
 }
 
 }  // namespace csa2

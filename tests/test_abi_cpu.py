@@ -163,3 +163,18 @@ def test_workspace_size():
     assert B.csa2_workspace_size(d, c, B.EP_LAYER_GROUP, 1) >= n
     with pytest.raises(B.Csa2Error):
         B.csa2_workspace_size(dims(d=3), c, B.EP_INDEX_TOPK, 1)
+
+
+def test_trace_api_without_launches():
+    from kv_cache_compression_csa2_amd import binding as B
+
+    assert B.csa2_kernel_name(3) == "scan_mfma_bf16_kernel"
+    assert B.csa2_kernel_name(5) == "select_kernel"
+    assert B.csa2_kernel_name(99) == "unknown"
+    lib = B.library()
+    assert lib.csa2_trace_enable(-1) == -1  # CSA2_ERR_INVALID_ARG
+    recs, dropped = B.csa2_trace_read(16)
+    assert recs == [] and dropped == 0
+    st = lib.csa2_trace_enable(4)  # no device here: a HIP error; with one: enabled
+    assert st in (0, -5)
+    assert lib.csa2_trace_enable(0) == 0

@@ -57,3 +57,55 @@ def test_determinism(runner):
     torch.cuda.synchronize()
     for (t0, o0), L in zip(first, step.layers):
         assert torch.equal(t0, L["topk"]) and torch.equal(o0, L["out"])
+
+
+def test_graph_replay(runner):
+    """A step captured in a HIP graph gives the eager step's outputs on every replay."""
+    import torch
+
+    wl = synth.get("group_small")
+    inp = synth.Inputs(wl)
+    step = runner.DeviceStep(wl, inp)
+    step.run()
+    torch.cuda.synchronize()
+    eager = [(L["topk"].clone(), L["out"].clone(), L["lse"].clone()) for L in step.layers]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step.run()
+    for rep in range(3):
+        for L in step.layers:  # eager work between replays
+            L["topk"].fill_(-7)
+            L["out"].zero_()
+            L["lse"].zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        print(f"[graph] replay {rep}", flush=True)
+        for (t0, o0, l0), L in zip(eager, step.layers):
+            assert torch.equal(t0, L["topk"]) and torch.equal(o0, L["out"]) and torch.equal(l0, L["lse"])
+
+
+def test_kernel_trace(runner):
+    """The kernel trace records one positive duration per launch, in launch order."""
+    import torch
+
+    from kv_cache_compression_csa2_amd import binding as B
+
+    wl = synth.get("hsi_small")
+    inp = synth.Inputs(wl)
+    step = runner.DeviceStep(wl, inp)
+    B.csa2_trace_enable(64)
+    try:
+        step.run()
+        step.run()
+        torch.cuda.synchronize()
+        recs, dropped = B.csa2_trace_read()
+    finally:
+        B.csa2_trace_enable(0)
+    assert dropped == 0 and len(recs) % 2 == 0 and len(recs) >= 8
+    names = [n for n, _ in recs]
+    half = len(names) // 2
+    assert names[:half] == names[half:]
+    assert names[0] == "compress_kernel" and any(n.startswith("scan_") for n in names)
+    assert "select_kernel" in names and any(n.startswith("attn_") for n in names)
+    assert all(ms > 0 for _, ms in recs)
