@@ -150,10 +150,11 @@ __global__ __launch_bounds__(kThreads) void attn_generic_kernel(
 //      operand of v_mfma_f32_16x16x16_bf16; P is the B operand exactly as the
 //      logits left it, and each lane keeps the head of its softmax state.
 // At the end the four waves' (reference max, sum, O) are combined through LDS
-// in a fixed order.  The head groups of a query are placed on one XCD
-// (workgroups are dealt to the 8 XCDs in turn) so they share the query's rows
-// in that L2.  With several row splits per (query, head group) each workgroup
-// writes its unnormalised output and (reference max, sum); attn_merge_kernel
+// in a fixed order.  The head groups of one (query, row split) are placed on
+// one XCD (workgroups are dealt to the 8 XCDs in turn) so they share those
+// rows in that L2, and the (query, split) pairs go round all 8 XCDs.  With
+// several row splits per (query, head group) each workgroup writes its
+// unnormalised output and (reference max, sum); attn_merge_kernel
 // combines them.
 
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
@@ -238,12 +239,15 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
     int tiles_per_split, int n_splits, uint16_t* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ part_o, float* __restrict__ part_ml) {
   extern __shared__ __align__(16) uint8_t lds[];
-  const int G = H / 16, U = n_splits * G;
+  // workgroup -> (query, split, head group): the G head groups of one
+  // (query, split) pair share an XCD (id % 8), the pairs go round the XCDs
+  const int G = H / 16;
   const int64_t wg = blockIdx.x, x8 = wg & 7, rest = wg >> 3;
-  const int u = int(rest % U);
-  const int64_t bq = (rest / U) * 8 + x8;
-  if (bq >= n_bq) return;  // padding workgroup (uniform)
-  const int split = u / G, hg = u % G;
+  const int hg = int(rest % G);
+  const int64_t pair = (rest / G) * 8 + x8;
+  if (pair >= n_bq * n_splits) return;  // padding workgroup (uniform)
+  const int64_t bq = pair / n_splits;
+  const int split = int(pair % n_splits);
   const int64_t b = bq / n_q, t = q_pos[bq];
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -595,7 +599,7 @@ AttnPlan plan_attn(const csa2_dims& dims, const csa2_kv_cache& cache, int32_t n_
   splits = splits > kMaxSplits ? kMaxSplits : splits;
   p.tiles_per_split = (p.n_tiles + splits - 1) / splits;
   p.n_splits = (p.n_tiles + p.tiles_per_split - 1) / p.tiles_per_split;
-  p.n_blocks = 8 * int64_t(p.n_splits) * G * ((n_bq + 7) / 8);
+  p.n_blocks = 8 * G * ((n_bq * p.n_splits + 7) / 8);
   return p;
 }
 
@@ -634,7 +638,9 @@ hipError_t launch_attn(const csa2_dims& dims, const csa2_kv_cache& cache, const 
     }
     auto kern = cache.kv_dtype != CSA2_FP4 ? attn_mfma_kernel<false, 32>
                 : (cache.main_group == 32 ? attn_mfma_kernel<true, 32> : attn_mfma_kernel<true, 16>);
-    hipError_t e = launch_kernel(cache.kv_dtype == CSA2_FP4 ? CSA2_KERNEL_ATTN_FP4 : CSA2_KERNEL_ATTN_BF16, kern,
+    const int32_t kid = cache.kv_dtype != CSA2_FP4 ? CSA2_KERNEL_ATTN_BF16
+                        : (cache.main_group == 32 ? CSA2_KERNEL_ATTN_FP4 : CSA2_KERNEL_ATTN_FP4_G16);
+    hipError_t e = launch_kernel(kid, kern,
                                  dim3(unsigned(p.n_blocks)), dim3(256), kAttnLds, stream, dims.n_heads, dims.topk,
                                  dims.window, dims.d_rope, cache.capacity, make_rope_table(dims),
                                  static_cast<const uint16_t*>(q), q_pos, n_q, int64_t(cache.batch) * n_q, topk,

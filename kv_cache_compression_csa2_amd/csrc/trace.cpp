@@ -125,9 +125,10 @@ const char* csa2_kernel_name(int32_t kernel) {
     case CSA2_KERNEL_SCAN_FP4: return "scan_mfma_fp4_kernel";
     case CSA2_KERNEL_SELECT: return "select_kernel";
     case CSA2_KERNEL_ATTN_GENERIC: return "attn_generic_kernel";
-    case CSA2_KERNEL_ATTN_BF16: return "attn_mfma_kernel<false>";
-    case CSA2_KERNEL_ATTN_FP4: return "attn_mfma_kernel<true>";
+    case CSA2_KERNEL_ATTN_BF16: return "attn_mfma_kernel<false, 32>";
+    case CSA2_KERNEL_ATTN_FP4: return "attn_mfma_kernel<true, 32>";
     case CSA2_KERNEL_ATTN_MERGE: return "attn_merge_kernel";
+    case CSA2_KERNEL_ATTN_FP4_G16: return "attn_mfma_kernel<true, 16>";
     default: return "unknown";
   }
 }
