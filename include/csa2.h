@@ -277,7 +277,8 @@ typedef enum csa2_kernel {
   CSA2_KERNEL_ATTN_BF16 = 7,      /* attn_mfma_kernel over a bf16 cache */
   CSA2_KERNEL_ATTN_FP4 = 8,       /* attn_mfma_kernel over an FP4 cache, scales per 32 */
   CSA2_KERNEL_ATTN_MERGE = 9,     /* attn_merge_kernel */
-  CSA2_KERNEL_ATTN_FP4_G16 = 10   /* attn_mfma_kernel over an FP4 cache, scales per 16 */
+  CSA2_KERNEL_ATTN_FP4_G16 = 10,  /* attn_mfma_kernel over an FP4 cache, scales per 16 */
+  CSA2_KERNEL_SCAN_PREFILL = 11   /* scan_prefill_kernel (many queries per sequence) */
 } csa2_kernel;
 
 typedef struct csa2_trace_record {

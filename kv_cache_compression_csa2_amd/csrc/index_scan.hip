@@ -255,6 +255,203 @@ __global__ __launch_bounds__(256, 2) void scan_mfma_fp4_kernel(
                        scores, bmax, sbmax, dom_cap);
 }
 
+// ------------------------------------------------------- query-blocked scan --
+//
+// Many queries per sequence (chunked prefill): the score contraction is a
+// GEMM per head, S_h = Q_h . K^T, whose K operand is shared by all 32 heads.
+// A workgroup (4 waves) owns 32 queries of one sequence and 512 entries; wave
+// w owns entries [128w, 128w+128).  Each wave loads its entries' indexer K
+// once, in registers, as the A operand of v_mfma_f32_32x32x16_bf16 (lane =
+// entry, 8 channels per lane and k-step; 4 blocks of 32 entries x 8 k-steps),
+// so the products are logits^T[entry][query]: a lane then holds one query and
+// runs of 4 consecutive entries, which makes the head weight one value per
+// lane, the score stores 16 bytes wide and a block maximum one exchange.
+// The heads then stream through LDS two at a time: the 32 queries' rows of
+// heads 2p and 2p+1 (2 x 8 KB) are copied global -> LDS (global_load_lds_dwordx4,
+// from inline assembly so the compiler does not drain them before LDS reads)
+// one pair ahead into a double buffer, and every wave contracts each head
+// against its resident K (8 k-steps x 4 blocks), then adds w_h * max(0, logit)
+// into its 32 x 128 scores - one head's additions run under the next head's
+// products (two accumulator sets).  One workgroup barrier per head pair.  The
+// query rows sit in LDS XOR-swizzled by 16-byte chunk so the B-operand reads
+// of 32 rows spread over the banks.
+// Scores, block maxima and super-block maxima are then written in the same
+// layout as the per-query scan.  The workgroups of one query block run on one
+// XCD (workgroups are dealt to the 8 XCDs in turn), entry blocks in order, so
+// the block's query rows stay in that L2 while K streams.
+
+constexpr int kPQ = 32;               // queries per query block
+constexpr int kQB = 1;                // query blocks per workgroup, in turn, sharing its resident K
+                                      // (more than one overflows the register file at this tile size)
+constexpr int kPE = 512;              // entries per workgroup
+constexpr int kQTile = kPQ * 256;     // one head's query rows (bytes)
+
+typedef float f32x16_t_ __attribute__((__vector_size__(64)));
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; naming it tells the compiler it changes
+// Copy 16 bytes per lane from global `src` to LDS byte address `lds_addr` +
+// 16 * lane.  Completion is tracked only by the caller's s_waitcnt vmcnt.
+__device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr), "v"(src) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// LDS slot (16 bytes) of chunk c (0..15) of query row q (0..31) in a head tile.
+__device__ __forceinline__ int qslot(int q, int c) { return q * 16 + (c ^ (q & 15)); }
+
+__global__ __launch_bounds__(256, 1) void scan_prefill_kernel(
+    int ratio, int64_t capacity, const uint16_t* __restrict__ idx_q, const float* __restrict__ head_w,
+    const int32_t* __restrict__ q_pos, int n_q, const uint8_t* __restrict__ idx_k,
+    const int32_t* __restrict__ n_entries, float* __restrict__ scores, float* __restrict__ bmax,
+    float* __restrict__ sbmax, int64_t dom_cap, int nqs, int neb, int groups) {
+  __shared__ __align__(16) uint8_t qtile[4][kQTile];  // 2 stages x 2 heads
+  __shared__ __align__(16) float wl[32][kPQ];  // head weights [head][query]
+  __shared__ int nvis[kPQ];
+  __shared__ int vis_max;
+
+  // workgroup -> (sequence, kQB query blocks, entry block): the entry blocks
+  // of one query group share an XCD (id % 8) and follow each other
+  const int64_t wg = blockIdx.x, x8 = wg & 7, rest = wg >> 3;
+  const int64_t grp = x8 + 8 * (rest / neb);
+  if (grp >= groups) return;  // padding workgroup (uniform)
+  const int eb = int(rest % neb);
+  const int b = int(grp / nqs), qbase = int(grp % nqs) * (kQB * kPQ);
+  const int tid = threadIdx.x, lane = tid & 63, n = lane & 31, hl = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t e_wg = int64_t(eb) * kPE, e0 = e_wg + 128 * wave;
+  const int64_t n_ent = clamp_entries(n_entries, b, capacity);
+
+  // ---- issue first, independent of the bookkeeping below: this wave's
+  // entries' indexer K (the A operand, resident for all heads) and the query
+  // tiles of heads 0 and 1 ----
+  uint4 kreg[4][8];
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+    int64_t e = e0 + 32 * blk + n;
+    e = e < capacity ? e : capacity - 1;  // slots past the cache: any valid row (masked below)
+    const uint4* p = reinterpret_cast<const uint4*>(idx_k + ((int64_t(b) * capacity + e) * 128 + 8 * hl) * 2);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) kreg[blk][s] = p[2 * s];  // channels 16s + 8hl .. +8
+  }
+  // copies of the query tiles of heads 2p and 2p+1 into stage p & 1: 16
+  // instructions of 1 KB (4 query rows each); wave w issues 4 of them
+  auto issue_pair = [&](int p, int q0) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane(
+        uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)qtile[2 * (p & 1)])));
+#pragma unroll
+    for (int m4 = 0; m4 < 4; ++m4) {
+      const int m = 4 * wave + m4;          // 0..15: head 2p + m / 8, instruction m % 8
+      const int hh = 2 * p + (m >> 3);
+      const int slot = (m & 7) * 64 + lane;  // destination slot in that head's tile
+      const int q = slot >> 4;               // query row of the slot
+      const int c = (slot & 15) ^ (q & 15);  // its chunk (inverse of qslot)
+      const int qg = min(q0 + q, n_q - 1);   // rows past the last query: any valid row (never stored)
+      const uint16_t* src = idx_q + ((int64_t(b) * n_q + qg) * 32 + hh) * 128 + 8 * c;
+      copy16_to_lds(src, base + m * 1024);
+    }
+  };
+#pragma unroll 1
+  for (int qs = 0; qs < kQB; ++qs) {
+    const int q0 = qbase + qs * kPQ;
+    if (q0 >= n_q) break;  // uniform
+    issue_pair(0, q0);
+
+    // ---- per-query visibility and head weights ----
+    __syncthreads();  // the previous block's readers of vis_max, nvis and wl are done
+    if (tid == 0) vis_max = 0;
+    __syncthreads();
+    if (tid < kPQ) {
+      const int q = q0 + tid;
+      const int v = q < n_q ? int(visible_count(n_ent, q_pos[int64_t(b) * n_q + q], ratio)) : 0;
+      nvis[tid] = v;
+      atomicMax(&vis_max, v);
+    }
+    for (int x = tid; x < 32 * kPQ; x += 256) {
+      const int hh = x / kPQ, qq = x % kPQ;
+      wl[hh][qq] = q0 + qq < n_q ? head_w[(int64_t(b) * n_q + q0 + qq) * 32 + hh] : 0.0f;
+    }
+    // every load so far (K included) complete, with a wait the compiler sees:
+    // from here on the kernel's own vmcnt waits count only head copies
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    const int64_t vmax = vis_max;
+    const bool wave_live = e0 < vmax;  // some query sees some entry of this wave's range
+
+    f32x16_t_ sacc[4];
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) sacc[blk] = f32x16_t_{};
+
+    if (e_wg < vmax) {
+      // logits of head hh from tile `qt` into acc
+      auto contract = [&](const uint8_t* qt, f32x16_t_* acc) {
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) acc[blk] = f32x16_t_{};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(qt + 16 * qslot(n, 2 * s + hl));
+#pragma unroll
+          for (int blk = 0; blk < 4; ++blk)
+            acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[blk][s]), a, acc[blk], 0, 0, 0);
+        }
+      };
+      // scores += w_hh * max(0, logit); max(0, x) as an integer max on the bits
+      auto fold = [&](int hh, const f32x16_t_* acc) {
+        const float w = wl[hh][n];
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            sacc[blk][r] += w * __int_as_float(max(__float_as_int(acc[blk][r]), 0));
+      };
+      f32x16_t_ acc_a[4], acc_b[4];
+      for (int p = 0; p < 16; ++p) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies of heads 2p, 2p+1
+        __syncthreads();  // every wave's copies landed; the other stage is free
+        if (p + 1 < 16) issue_pair(p + 1, q0);
+        if (!wave_live) continue;
+        const uint8_t* qt = qtile[2 * (p & 1)];
+        contract(qt, acc_a);                       // head 2p
+        if (p > 0) fold(2 * p - 1, acc_b);         // head 2p-1, under head 2p's products
+        contract(qt + kQTile, acc_b);              // head 2p+1
+        fold(2 * p, acc_a);                        // head 2p, under head 2p+1's products
+      }
+      if (wave_live) fold(31, acc_b);
+    }
+
+    // ---- mask, store scores and maxima ----
+    // lane: query n, entries e0 + 32 blk + 8j + 4hl + i (i < 4) in sacc[blk][4j + i]
+    if (e0 >= dom_cap) continue;  // uniform per wave
+    const int q = q0 + n;
+    const int64_t row = int64_t(b) * n_q + q;
+    const int64_t vis = nvis[n];
+    const int64_t nsb = dom_cap / 64;
+    float m_sb[2] = {-INFINITY, -INFINITY};
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t e = e0 + 32 * blk + 8 * j + 4 * hl;
+        float4 v;
+        v.x = e < vis ? sacc[blk][4 * j] : -INFINITY;
+        v.y = e + 1 < vis ? sacc[blk][4 * j + 1] : -INFINITY;
+        v.z = e + 2 < vis ? sacc[blk][4 * j + 2] : -INFINITY;
+        v.w = e + 3 < vis ? sacc[blk][4 * j + 3] : -INFINITY;
+        if (q < n_q) *reinterpret_cast<float4*>(scores + row * dom_cap + e) = v;
+        float m = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
+        m = fmaxf(m, __shfl_xor(m, 32, kWave));  // the block's other 4 entries
+        if (q < n_q && hl == 0) bmax[row * (dom_cap / 8) + (e0 + 32 * blk + 8 * j) / 8] = m;
+        m_sb[blk >> 1] = fmaxf(m_sb[blk >> 1], m);
+      }
+    }
+#pragma unroll
+    for (int p2 = 0; p2 < 2; ++p2) {
+      const int64_t sb = (e0 + 64 * p2) / 64;
+      if (q < n_q && hl == 0 && sb < nsb) sbmax[row * nsb + sb] = m_sb[p2];
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_scan(const csa2_dims& dims, const csa2_kv_cache& cache, const void* idx_q, const float* head_w,
@@ -262,6 +459,18 @@ hipError_t launch_scan(const csa2_dims& dims, const csa2_kv_cache& cache, const 
                        hipStream_t stream) {
   const bool mfma_shape = dims.n_idx_heads == 32 && dims.d_idx == 128 && dims.act_dtype == CSA2_BF16 &&
                           (cache.kv_dtype == CSA2_BF16 || (cache.kv_dtype == CSA2_FP4 && cache.idx_group == 32));
+  if (mfma_shape && cache.kv_dtype == CSA2_BF16 && !pool_in && n_q >= 8) {
+    // many queries per sequence: query-blocked MFMA scan
+    const int nqs = (n_q + kQB * kPQ - 1) / (kQB * kPQ);
+    const int neb = int((ss.dom_cap + kPE - 1) / kPE);
+    const int64_t groups = int64_t(cache.batch) * nqs;
+    const int64_t blocks = 8 * int64_t(neb) * ((groups + 7) / 8);
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    return launch_kernel(CSA2_KERNEL_SCAN_PREFILL, scan_prefill_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream,
+                         cache.ratio, cache.capacity, static_cast<const uint16_t*>(idx_q), head_w, q_pos, n_q,
+                         static_cast<const uint8_t*>(cache.idx_k), cache.n_entries, ss.scores, ss.bmax, ss.sbmax,
+                         ss.dom_cap, nqs, neb, int(groups));
+  }
   if (mfma_shape) {
     const int64_t nsb = ss.dom_cap / 64;
     const dim3 grid(unsigned((nsb + 4 * kSbPerWave - 1) / (4 * kSbPerWave)), n_q, cache.batch);
