@@ -36,6 +36,9 @@ extern "C" __device__ uint32_t __ockl_wfred_max_u32(uint32_t);
 namespace csa2 {
 namespace {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
 constexpr int kNT = 1024;
 constexpr int kNW = kNT / kWave;
 constexpr int kMaxCand = 16384;
@@ -47,7 +50,7 @@ struct SelLds {
   lds_u32* keys;  // [kMaxCand] candidate keys by position
   lds_u32* la;    // [kMaxList]
   lds_u32* lb;    // [kMaxList]
-  lds_u32* hist;  // [kBins], all zero between passes
+  lds_u32* hist;  // [4 * kBins], four copies, all zero between passes
   lds_u32* wred;  // [4 * kNW] per-wave partial results
   lds_u32* misc;  // [8]
 };
@@ -72,30 +75,39 @@ __device__ __forceinline__ uint32_t waves_before(const SelLds L, int base, int w
 
 // Select the best min(m, #valid) of keys[0..n) (valid: key > kKeyNegInf),
 // ties to the lower position; write the chosen positions ascending to out[].
-// Returns the number chosen.  All threads of the block must call it; hist is
-// zero on entry and on exit.
+// Returns the number chosen.  All threads of the block must call it; the
+// histograms are zero on entry and on exit.
 //
-// The threshold key T is found by narrowing a key interval [lo, hi] that
-// holds it: each pass splits the interval into at most 2048 equal bins, and
-// the interval shrinks to the bin that holds the need-th largest key.
-// Starting from the observed [min, max] of the keys spreads similar scores
-// over many bins, so the LDS histogram atomics rarely collide; three passes
-// always suffice for 32-bit keys.  Wave w owns positions [w*seg, w*seg+seg)
-// and bins [128w, 128w+128); all loops are short and rolled, since a single
-// wave retires dependent instructions slowly and this step is latency-bound.
+// Thread t owns the run of R consecutive positions [R t, R t + R) (R a
+// multiple of 4, at most 16), read 16 bytes at a time.  The threshold key T
+// is found by narrowing a key interval [lo, hi] that holds it: each pass
+// splits the interval into at most 2048 equal bins, and the interval shrinks
+// to the bin that holds the need-th largest key; when that bin is taken
+// whole the search stops early.  Starting from the observed [min, max] of the
+// keys spreads similar scores over many bins, and four copies of the
+// histogram (by wave) cut the LDS atomic collisions of clustered keys; three
+// passes always suffice for 32-bit keys.  The compaction is one block-wide
+// scan of packed (greater, equal) counts, then a short walk per thread.
 __device__ int select_top(const SelLds L, int n, int m, lds_u32* out) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int seg = (((n + kNW - 1) / kNW) + 63) & ~63;
-  const int lo_p = w * seg, hi_p = min(n, lo_p + seg);
+  const int R = ((((n + kNT - 1) / kNT) + 3) & ~3);
+  const int p0 = R * tid;
+  lds_u32* const hist = L.hist + kBins * (w & 3);
 
   // count, min and max of the valid keys
   uint32_t cnt = 0, kmn = 0xFFFFFFFFu, kmx = 0u;
-  for (int p = lo_p + lane; p < hi_p; p += kWave) {
-    const uint32_t k = L.keys[p];
-    if (k > kKeyNegInf) {
-      ++cnt;
-      kmn = min(kmn, k);
-      kmx = max(kmx, k);
+  for (int v = 0; v < R; v += 4) {
+    if (p0 + v >= n) break;
+    const u32x4 k4 = *reinterpret_cast<const lds_u32x4*>(L.keys + p0 + v);
+    const uint32_t kk[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t k = p0 + v + i < n ? kk[i] : kKeyNegInf;
+      if (k > kKeyNegInf) {
+        ++cnt;
+        kmn = min(kmn, k);
+        kmx = max(kmx, k);
+      }
     }
   }
   cnt = __ockl_wfred_add_u32(cnt);
@@ -118,16 +130,27 @@ __device__ int select_top(const SelLds L, int n, int m, lds_u32* out) {
       const uint64_t width = uint64_t(hi) - lo + 1;
       const int bits = 64 - __clzll(width - 1);  // bits spanned by the interval
       const int shift = bits > 11 ? bits - 11 : 0;
-      for (int p = lo_p + lane; p < hi_p; p += kWave) {
-        const uint32_t k = L.keys[p];
-        if (k > kKeyNegInf && k >= lo && k <= hi) lds_inc(&L.hist[(k - lo) >> shift]);
+      for (int v = 0; v < R; v += 4) {
+        if (p0 + v >= n) break;
+        const u32x4 k4 = *reinterpret_cast<const lds_u32x4*>(L.keys + p0 + v);
+        const uint32_t kk[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t k = kk[i];
+          if (p0 + v + i < n && k > kKeyNegInf && k >= lo && k <= hi) lds_inc(&hist[(k - lo) >> shift]);
+        }
       }
       __syncthreads();
-      // bins [128w, 128w+128): lane holds bins b0 = 128w + 2*lane and b0 + 1
+      // bins [128w, 128w+128): lane holds bins b0 = 128w + 2*lane and b0 + 1 (four copies summed)
       const int b0 = kBinsPerWave * w + 2 * lane;
-      const uint32_t h0 = L.hist[b0], h1 = L.hist[b0 + 1];
-      L.hist[b0] = 0;
-      L.hist[b0 + 1] = 0;
+      uint32_t h0 = 0, h1 = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        h0 += L.hist[kBins * c + b0];
+        h1 += L.hist[kBins * c + b0 + 1];
+        L.hist[kBins * c + b0] = 0;
+        L.hist[kBins * c + b0 + 1] = 0;
+      }
       const uint32_t s = h0 + h1;
       const uint32_t incl = __ockl_wfscan_add_u32(s, true);
       const uint32_t wtot = uint32_t(__builtin_amdgcn_readlane(int(incl), kWave - 1));
@@ -142,55 +165,72 @@ __device__ int select_top(const SelLds L, int n, int m, lds_u32* out) {
         if (need <= above + h1) {
           L.misc[0] = uint32_t(b0 + 1);
           L.misc[1] = need - above;
+          L.misc[2] = h1;
         } else {
           L.misc[0] = uint32_t(b0);
           L.misc[1] = need - above - h1;
+          L.misc[2] = h0;
         }
       }
       __syncthreads();
-      const uint32_t bin = L.misc[0];
+      const uint32_t bin = L.misc[0], in_bin = L.misc[2];
       need = L.misc[1];
       __syncthreads();
       const uint64_t new_lo = uint64_t(lo) + (uint64_t(bin) << shift);
       hi = uint32_t(min(uint64_t(hi), new_lo + (uint64_t(1) << shift) - 1));
       lo = uint32_t(new_lo);
-      if (shift == 0) break;  // a single key value: the threshold
+      if (need == in_bin) {  // the whole bin is taken: every key >= lo, no ties to break
+        T = lo - 1;          // lo > kKeyNegInf, so T >= kKeyNegInf
+        need = 0;
+        break;
+      }
+      if (shift == 0) {  // a single key value: the threshold
+        T = lo;
+        break;
+      }
     }
-    T = lo;
   }
 
-  // order-preserving compaction: ties at T go to the lowest positions
+  // order-preserving compaction: (greater, equal) counts packed 16:16, one block scan
   uint32_t gt = 0, eq = 0;
-  for (int p = lo_p + lane; p < hi_p; p += kWave) {
-    const uint32_t k = L.keys[p];
-    gt += k > T;
-    eq += (k == T) && (k > kKeyNegInf);
+  for (int v = 0; v < R; v += 4) {
+    if (p0 + v >= n) break;
+    const u32x4 k4 = *reinterpret_cast<const lds_u32x4*>(L.keys + p0 + v);
+    const uint32_t kk[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t k = p0 + v + i < n ? kk[i] : kKeyNegInf;
+      gt += k > T && k > kKeyNegInf;
+      eq += k == T && k > kKeyNegInf;
+    }
   }
-  gt = __ockl_wfred_add_u32(gt);
-  eq = __ockl_wfred_add_u32(eq);
-  if (lane == 0) {
-    L.wred[w] = gt;
-    L.wred[kNW + w] = eq;
-  }
+  const uint32_t packed = (gt << 16) | eq;
+  const uint32_t incl = __ockl_wfscan_add_u32(packed, true);
+  if (lane == kWave - 1) L.wred[w] = incl;
   __syncthreads();
-  const uint32_t eq_base = waves_before(L, kNW, w);
-  const uint32_t take_w = need > eq_base ? min(eq, need - eq_base) : 0u;
-  if (lane == 0) L.wred[2 * kNW + w] = gt + take_w;
-  __syncthreads();
-  const uint32_t sel_base = waves_before(L, 2 * kNW, w);
-  const uint32_t chosen = reduce_waves(L, 2 * kNW, 0);
-  const uint64_t ltm = (uint64_t(1) << lane) - 1;
-  uint32_t run_eq = 0, run_sel = 0;
-  for (int base = lo_p; base < lo_p + seg; base += kWave) {
-    const int p = base + lane;
-    const uint32_t k = p < hi_p ? L.keys[p] : 0u;
-    const bool is_eq = (k == T) && (k > kKeyNegInf);
-    const uint64_t eqm = __ballot(is_eq);
-    const bool sel = k > T || (is_eq && eq_base + run_eq + __popcll(eqm & ltm) < need);
-    const uint64_t selm = __ballot(sel);
-    if (sel) out[sel_base + run_sel + __popcll(selm & ltm)] = uint32_t(p);
-    run_eq += __popcll(eqm);
-    run_sel += __popcll(selm);
+  const uint32_t wv = lane < kNW ? L.wred[lane] : 0u;
+  const uint32_t wincl = __ockl_wfscan_add_u32(wv, true);
+  const uint32_t before_w = w == 0 ? 0u : uint32_t(__builtin_amdgcn_readlane(int(wincl), w - 1));
+  const uint32_t all = uint32_t(__builtin_amdgcn_readlane(int(wincl), kNW - 1));
+  const uint32_t before = before_w + incl - packed;
+  uint32_t gt_run = before >> 16, eq_run = before & 0xFFFFu;
+  const uint32_t chosen = (all >> 16) + min(all & 0xFFFFu, need);
+  for (int v = 0; v < R; v += 4) {
+    if (p0 + v >= n) break;
+    const u32x4 k4 = *reinterpret_cast<const lds_u32x4*>(L.keys + p0 + v);
+    const uint32_t kk[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t k = p0 + v + i < n ? kk[i] : kKeyNegInf;
+      if (k <= kKeyNegInf) continue;
+      if (k > T) {
+        out[gt_run + min(eq_run, need)] = uint32_t(p0 + v + i);
+        ++gt_run;
+      } else if (k == T) {
+        if (eq_run < need) out[gt_run + eq_run] = uint32_t(p0 + v + i);
+        ++eq_run;
+      }
+    }
   }
   __syncthreads();
   return int(chosen);
@@ -242,9 +282,9 @@ __global__ __launch_bounds__(kNT) void select_kernel(int topk, int cand_blocks, 
   L.la = L.keys + kMaxCand;
   L.lb = L.la + kMaxList;
   L.hist = L.lb + kMaxList;
-  L.wred = L.hist + kBins;
+  L.wred = L.hist + 4 * kBins;
   L.misc = L.wred + 4 * kNW;
-  for (int x = threadIdx.x; x < kBins; x += kNT) L.hist[x] = 0;
+  for (int x = threadIdx.x; x < 4 * kBins; x += kNT) L.hist[x] = 0;
 
   const int qi = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int64_t row = int64_t(b) * n_q + qi;
@@ -338,7 +378,7 @@ __global__ __launch_bounds__(kNT) void select_kernel(int topk, int cand_blocks, 
   }
 }
 
-constexpr size_t kSelectLds = sizeof(uint32_t) * (kMaxCand + 2 * kMaxList + kBins + 4 * kNW + 8);
+constexpr size_t kSelectLds = sizeof(uint32_t) * (kMaxCand + 2 * kMaxList + 4 * kBins + 4 * kNW + 8);
 
 }  // namespace
 
