@@ -81,178 +81,245 @@ __global__ __launch_bounds__(kThreads) void scan_generic_kernel(
 //
 // Production shape: 32 indexer heads x 128, bf16 queries, bf16 or FP4 (one
 // E4M3 scale per 32 channels) indexer K.  The per-tile contraction
-// S[head][entry] = Q[32 x 128] . K^T[128 x 32] runs as eight
-// v_mfma_f32_32x32x16_bf16.  Operands come straight from memory in MFMA
-// layout: lane l supplies row (l % 32) with eight consecutive k of its half
-// (l / 32); the order in which k is visited is free, so it is chosen to make
-// each lane's K bytes contiguous (bf16: one 128-byte run per lane) or to keep
-// every step inside one FP4 scale group (FP4: the group scale is applied to
-// the step-group's partial sum after the MFMA, because the hardware's scaled
-// FP4 convert honours only the exponent of its scale).  Accumulator lane l
-// register r holds head 8*(r/4) + 4*(l/32) + r%4 of entry l % 32; the head
-// sum w_h * ReLU(.) runs in registers, then one cross-half shuffle completes
-// the entry score.
+// S[head][entry] = Q[32 x 128] . K^T[128 x 32] runs as eight 32x32x16 MFMAs.
+// Operands come straight from memory in MFMA layout: lane l supplies row
+// (l % 32) with eight consecutive k of its half (l / 32); the order in which
+// k is visited is free, so it is chosen to make each lane's K bytes
+// contiguous: bf16, one 128-byte run per lane; FP4, two 16-byte runs, each
+// one whole scale group (lane half h takes groups h and 2 + h, so the two
+// halves of one k-step may belong to different groups, which the exact
+// per-element dequantisation below allows).  Accumulator lane l register r holds head
+// 8*(r/4) + 4*(l/32) + r%4 of entry l % 32; the head sum w_h * ReLU(.) runs in
+// registers, then one cross-half shuffle completes the entry score.
 //
-// A workgroup (4 waves) covers 16 super-blocks of 64 domain slots; wave w
-// takes super-blocks w, w+4, w+8, w+12, two 32-entry tiles each.
+// FP4 runs on the fp16 MFMA with every K element dequantised exactly: an
+// E2M1 value times an E4M3 scale has at most 6 significant bits and lies in
+// [2^-10, 2688], so it is an fp16 normal.  The scaled FP4 convert applies
+// the scale's power of two (it reads only the exponent of its scale
+// operand), and one packed fp16 multiply by the scale's significand (1.mmm)
+// finishes each pair exactly.  The query goes to fp16 times 2^k, with k
+// chosen from the query's largest magnitude so that it lands in [2^14, 2^15)
+// (exact for every element down to 2^-28 of that magnitude; smaller ones
+// fall to fp16 subnormals, whose rounding, at most 2^-24 of 2^k, is far below
+// the float32 accumulation error); ReLU commutes with the positive factor,
+// so the score is multiplied by 2^-k at the end, exactly.
+//
+// A workgroup (4 waves) covers 4 kSbW super-blocks of 64 domain slots; wave
+// w takes super-blocks w, w+4, ... (two 32-entry tiles each), kBatch at a
+// time, with the loads of the next batch issued before the current one is
+// contracted.  The batches are fully unrolled so the two load buffers are
+// fixed registers.  POOL: the domain is a block pool (slot -> pool entry).
+
+extern "C" __device__ uint32_t __ockl_wfred_max_u32(uint32_t);
 
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
-typedef __bf16 bf16x2_t __attribute__((__vector_size__(4)));
+typedef _Float16 f16x8_t __attribute__((__vector_size__(16)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((__vector_size__(64)));
 
 constexpr int kSbPerWave = 4;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-// Eight E2M1 codes (one dword, low nibble first) -> eight exact bf16 values.
-__device__ __forceinline__ bf16x8_t fp4x8_to_bf16(uint32_t w) {
-  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0);
-  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1);
-  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2);
-  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3);
+// Eight E2M1 codes (one dword, low nibble first) times the E4M3 scale s ->
+// eight exact fp16 values; mpair holds s's significand twice (fp16).
+__device__ __forceinline__ f16x8_t fp4x8_to_f16(uint32_t w, float s, uint32_t mpair) {
+  const f16x2_t m = __builtin_bit_cast(f16x2_t, mpair);
   uint4 v;
-  v.x = __builtin_bit_cast(uint32_t, a);
-  v.y = __builtin_bit_cast(uint32_t, b);
-  v.z = __builtin_bit_cast(uint32_t, c);
-  v.w = __builtin_bit_cast(uint32_t, d);
-  return as_bf16x8(v);
+  v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 0) * m);
+  v.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 1) * m);
+  v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 2) * m);
+  v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 3) * m);
+  return __builtin_bit_cast(f16x8_t, v);
 }
 
-template <bool FP4>
+// The significand 1.mmm of a positive float (its value over its power of
+// two) as a pair of fp16 values; exact for the E4M3 scale values.
+__device__ __forceinline__ uint32_t significand_pair(float s) {
+  const uint32_t h = ((__float_as_uint(s) >> 13) & 0x3FFu) | 0x3C00u;
+  return h | (h << 16);
+}
+
+// max(x, 0) as an integer max on the bits (fmaxf adds a canonicalising max)
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// Tile loads of one batch (kBatch super-blocks = 2 kBatch tiles of 32 entries).
+template <bool FP4, int kBatch>
+struct ScanBatch {
+  int32_t slot[2 * kBatch];
+  bool valid[2 * kBatch];
+  uint4 kb[FP4 ? 1 : 2 * kBatch][8];
+  uint4 kf[FP4 ? 2 * kBatch : 1][2];
+  uint32_t ks[FP4 ? 2 * kBatch : 1];
+};
+
+template <bool FP4, bool POOL, int kBatch, int kSbW>
 __device__ __forceinline__ void scan_mfma_body(
     int ratio, int64_t capacity, const uint16_t* __restrict__ idx_q, const float* __restrict__ head_w,
     const int32_t* __restrict__ q_pos, int n_q, const int32_t* __restrict__ pool_in, int cand_blocks,
     const uint8_t* __restrict__ idx_k, const uint8_t* __restrict__ idx_scale, const int32_t* __restrict__ n_entries,
     float* __restrict__ scores, float* __restrict__ bmax, float* __restrict__ sbmax, int64_t dom_cap) {
-  constexpr int kBatch = FP4 ? 4 : 1;  // super-blocks whose loads are issued together
   constexpr int kTiles = 2 * kBatch;
+  constexpr int kIters = kSbW / kBatch;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 31, h = lane >> 5;
   const int qi = blockIdx.y, b = blockIdx.z;
   const int64_t row = int64_t(b) * n_q + qi;
-  const int64_t nsb = dom_cap / 64;
-  const int64_t n_vis = visible_count(clamp_entries(n_entries, b, capacity), q_pos[row], ratio);
+  const int nsb = int(dom_cap / 64);
+  const int n_vis = int(visible_count(clamp_entries(n_entries, b, capacity), q_pos[row], ratio));
+  const int sb0 = int(blockIdx.x) * (4 * kSbW) + wave;
+  // this sequence's rows (bf16: 256 bytes, FP4: 64 code bytes + 4 scale bytes)
+  const uint8_t* kseq = idx_k + int64_t(b) * capacity * (FP4 ? 64 : 256);
+  const uint8_t* sseq = FP4 ? idx_scale + int64_t(b) * capacity * 4 : nullptr;
+  const int32_t* prow = POOL ? pool_in + row * cand_blocks : nullptr;
+  float* srow = scores + row * dom_cap;
+  float* brow = bmax + row * (dom_cap / 8);
+  float* sbrow = sbmax + row * nsb;
+
+  auto issue = [&](int it, ScanBatch<FP4, kBatch>& B) {
+    const int sb_first = sb0 + 4 * kBatch * it;
+    const bool any_visible = sb_first < nsb && (POOL || sb_first * 64 < n_vis);
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+      const int sb = sb_first + 4 * (t >> 1);
+      B.slot[t] = sb * 64 + 32 * (t & 1) + n;
+      int j = B.slot[t];
+      if constexpr (POOL) {
+        const int blk = sb < nsb && B.slot[t] / 8 < cand_blocks ? prow[B.slot[t] / 8] : -1;
+        j = blk >= 0 ? blk * 8 + (B.slot[t] & 7) : -1;
+      }
+      B.valid[t] = sb < nsb && j >= 0 && j < n_vis;
+      const int jj = B.valid[t] ? j : 0;
+      if (any_visible) {
+        if constexpr (FP4) {
+          const uint8_t* p = kseq + int64_t(jj) * 64 + 16 * h;
+#pragma unroll
+          for (int g2 = 0; g2 < 2; ++g2) B.kf[t][g2] = *reinterpret_cast<const uint4*>(p + 32 * g2);
+          B.ks[t] = *reinterpret_cast<const uint32_t*>(sseq + int64_t(jj) * 4) >> (8 * h);
+        } else {
+          const uint4* p = reinterpret_cast<const uint4*>(kseq + int64_t(jj) * 256 + 128 * h);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) B.kb[t][q] = p[q];
+        }
+      }
+    }
+  };
+
+  ScanBatch<FP4, kBatch> buf[2];
+  issue(0, buf[0]);
 
   // A operand (indexer query) and the lane's 16 head weights, held for the whole scan
-  bf16x8_t qop[8];
   const uint16_t* qrow = idx_q + (row * 32 + n) * 128;
+  uint4 qraw[8];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const int k0 = FP4 ? 32 * (s >> 1) + 16 * h + 8 * (s & 1) : 64 * h + 8 * s;
-    qop[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + k0));
+  for (int q = 0; q < 8; ++q) {
+    const int k0 = FP4 ? 64 * (q >> 2) + 32 * h + 8 * (q & 3) : 64 * h + 8 * q;
+    qraw[q] = *reinterpret_cast<const uint4*>(qrow + k0);
   }
   float wreg[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) wreg[r] = head_w[row * 32 + 8 * (r >> 2) + 4 * h + (r & 3)];
-
-  const int64_t sb0 = int64_t(blockIdx.x) * (4 * kSbPerWave) + wave;
-  for (int it = 0; it < kSbPerWave; it += kBatch) {
-    const int64_t sb_first = sb0 + 4 * it;
-    if (sb_first >= nsb) break;
-    const bool any_visible = pool_in || sb_first * 64 < n_vis;
-
-    // ---- issue the loads of kTiles tiles ----
-    int64_t slot[kTiles];
-    bool valid[kTiles];
-    uint4 kb[FP4 ? 1 : kTiles][8];
-    uint2 kf[FP4 ? kTiles : 1][4];
-    uint32_t ks[FP4 ? kTiles : 1];
+  bf16x8_t qop[FP4 ? 1 : 8];
+  f16x8_t qop16[FP4 ? 8 : 1];
+  float unscale = 1.0f;
+  if constexpr (FP4) {
+    uint32_t amax = 0;  // largest |q| of the query (bits of a non-negative float)
 #pragma unroll
-    for (int t = 0; t < kTiles; ++t) {
-      const int64_t sb = sb_first + 4 * (t >> 1);
-      slot[t] = sb * 64 + 32 * (t & 1) + n;
-      int64_t j = -1;
-      if (sb < nsb && any_visible) {
-        if (pool_in) {
-          const int64_t blk = slot[t] / 8 < cand_blocks ? pool_in[row * cand_blocks + slot[t] / 8] : -1;
-          if (blk >= 0) j = blk * 8 + (slot[t] & 7);
-        } else {
-          j = slot[t];
-        }
-      }
-      valid[t] = j >= 0 && j < n_vis;
-      const int64_t crow = int64_t(b) * capacity + (valid[t] ? j : 0);
-      if (any_visible) {
-        if (FP4) {
-          const uint8_t* p = idx_k + crow * 64 + 8 * h;
+    for (int q = 0; q < 8; ++q) {
+      const uint32_t w4[4] = {qraw[q].x, qraw[q].y, qraw[q].z, qraw[q].w};
 #pragma unroll
-          for (int g = 0; g < 4; ++g) kf[t][g] = *reinterpret_cast<const uint2*>(p + 16 * g);
-          ks[t] = *reinterpret_cast<const uint32_t*>(idx_scale + crow * 4);
-        } else {
-          const uint4* p = reinterpret_cast<const uint4*>(idx_k + (crow * 128 + 64 * h) * 2);
-#pragma unroll
-          for (int s = 0; s < 8; ++s) kb[t][s] = p[s];
-        }
-      }
+      for (int i = 0; i < 4; ++i) amax = max(amax, max((w4[i] << 16) & 0x7FFF0000u, w4[i] & 0x7FFF0000u));
     }
+    amax = __ockl_wfred_max_u32(amax);
+    const int e = amax ? int(amax >> 23) - 127 : 0;  // floor(log2 max|q|)
+    const int k = min(100, max(-100, 14 - e));
+    const float up = __uint_as_float(uint32_t(127 + k) << 23);
+    unscale = __uint_as_float(uint32_t(127 - k) << 23);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint32_t w4[4] = {qraw[q].x, qraw[q].y, qraw[q].z, qraw[q].w};
+      uint4 v;
+      uint32_t* vv = reinterpret_cast<uint32_t*>(&v);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f16x2_t pr = {_Float16(__uint_as_float(w4[i] << 16) * up), _Float16(__uint_as_float(w4[i] & 0xFFFF0000u) * up)};
+        vv[i] = __builtin_bit_cast(uint32_t, pr);
+      }
+      qop16[q] = __builtin_bit_cast(f16x8_t, v);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) qop[q] = as_bf16x8(qraw[q]);
+  }
 
-    // ---- contract, reduce over heads, write scores and maxima ----
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    if (it + 1 < kIters) issue(it + 1, buf[(it + 1) & 1]);
+    ScanBatch<FP4, kBatch>& B = buf[it & 1];
+    const int sb_first = sb0 + 4 * kBatch * it;
+    const bool any_visible = sb_first < nsb && (POOL || sb_first * 64 < n_vis);
     float tmax[kTiles];
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
       float part = 0.0f;
       if (any_visible) {
-        if (FP4) {
-          f32x16_t acc[4];
+        f32x16_t acc = f32x16_t{};
+        if constexpr (FP4) {
+          // this lane's groups: h (first 16 bytes) and 2 + h (second)
+          const float sg[2] = {__builtin_amdgcn_cvt_f32_fp8(int(B.ks[t]), 0), __builtin_amdgcn_cvt_f32_fp8(int(B.ks[t]), 2)};
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            acc[g] = f32x16_t{};
-            acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qop[2 * g], fp4x8_to_bf16(kf[t][g].x), acc[g], 0, 0, 0);
-            acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qop[2 * g + 1], fp4x8_to_bf16(kf[t][g].y), acc[g], 0, 0, 0);
-          }
-          const float s0 = e4m3_to_f32(ks[t] & 0xFF), s1 = e4m3_to_f32((ks[t] >> 8) & 0xFF);
-          const float s2 = e4m3_to_f32((ks[t] >> 16) & 0xFF), s3 = e4m3_to_f32(ks[t] >> 24);
+          for (int g2 = 0; g2 < 2; ++g2) {
+            const uint32_t mp = significand_pair(sg[g2]);
+            const uint32_t w4[4] = {B.kf[t][g2].x, B.kf[t][g2].y, B.kf[t][g2].z, B.kf[t][g2].w};
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float dot = s0 * acc[0][r] + s1 * acc[1][r] + s2 * acc[2][r] + s3 * acc[3][r];
-            part += wreg[r] * fmaxf(dot, 0.0f);
+            for (int sub = 0; sub < 4; ++sub)
+              acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qop16[4 * g2 + sub], fp4x8_to_f16(w4[sub], sg[g2], mp), acc, 0, 0, 0);
           }
         } else {
-          f32x16_t acc = f32x16_t{};
 #pragma unroll
-          for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qop[s], as_bf16x8(kb[t][s]), acc, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) part += wreg[r] * fmaxf(acc[r], 0.0f);
+          for (int q = 0; q < 8; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qop[q], as_bf16x8(B.kb[t][q]), acc, 0, 0, 0);
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) part += wreg[r] * relu(acc[r]);
       }
-      float sc = part + __shfl_xor(part, 32, kWave);
-      if (!valid[t]) sc = -INFINITY;
-      const int64_t sb = sb_first + 4 * (t >> 1);
-      if (sb < nsb && h == 0) scores[row * dom_cap + slot[t]] = sc;
+      float sc = (part + __shfl_xor(part, 32, kWave)) * unscale;
+      if (!B.valid[t]) sc = -INFINITY;
+      const int sb = sb_first + 4 * (t >> 1);
+      if (sb < nsb && h == 0) srow[B.slot[t]] = sc;
       float m = fmaxf(sc, __shfl_xor(sc, 1, kWave));
       m = fmaxf(m, __shfl_xor(m, 2, kWave));
       m = fmaxf(m, __shfl_xor(m, 4, kWave));
-      if (sb < nsb && h == 0 && (n & 7) == 0) bmax[row * (dom_cap / 8) + slot[t] / 8] = m;
+      if (sb < nsb && h == 0 && (n & 7) == 0) brow[B.slot[t] / 8] = m;
       m = fmaxf(m, __shfl_xor(m, 8, kWave));
       m = fmaxf(m, __shfl_xor(m, 16, kWave));
       tmax[t] = m;
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const int64_t sb = sb_first + 4 * u;
-      if (sb < nsb && lane == 0) sbmax[row * nsb + sb] = fmaxf(tmax[2 * u], tmax[2 * u + 1]);
+      const int sb = sb_first + 4 * u;
+      if (sb < nsb && lane == 0) sbrow[sb] = fmaxf(tmax[2 * u], tmax[2 * u + 1]);
     }
   }
 }
 
-// bf16 keeps one tile pair in flight per wave and fits 3 waves per SIMD;
-// FP4 keeps four pairs in flight (its rows are a quarter the size) at 2.
-__global__ __launch_bounds__(256, 3) void scan_mfma_bf16_kernel(
-    int ratio, int64_t capacity, const uint16_t* __restrict__ idx_q, const float* __restrict__ head_w,
-    const int32_t* __restrict__ q_pos, int n_q, const int32_t* __restrict__ pool_in, int cand_blocks,
-    const uint8_t* __restrict__ idx_k, const uint8_t* __restrict__ idx_scale, const int32_t* __restrict__ n_entries,
-    float* __restrict__ scores, float* __restrict__ bmax, float* __restrict__ sbmax, int64_t dom_cap) {
-  scan_mfma_body<false>(ratio, capacity, idx_q, head_w, q_pos, n_q, pool_in, cand_blocks, idx_k, idx_scale, n_entries,
-                        scores, bmax, sbmax, dom_cap);
-}
+#define SCAN_ARGS                                                                                                     \
+  int ratio, int64_t capacity, const uint16_t *__restrict__ idx_q, const float *__restrict__ head_w,                 \
+      const int32_t *__restrict__ q_pos, int n_q, const int32_t *__restrict__ pool_in, int cand_blocks,               \
+      const uint8_t *__restrict__ idx_k, const uint8_t *__restrict__ idx_scale,                                       \
+      const int32_t *__restrict__ n_entries, float *__restrict__ scores, float *__restrict__ bmax,                    \
+      float *__restrict__ sbmax, int64_t dom_cap
+#define SCAN_PASS \
+  ratio, capacity, idx_q, head_w, q_pos, n_q, pool_in, cand_blocks, idx_k, idx_scale, n_entries, scores, bmax, sbmax, dom_cap
 
-__global__ __launch_bounds__(256, 2) void scan_mfma_fp4_kernel(
-    int ratio, int64_t capacity, const uint16_t* __restrict__ idx_q, const float* __restrict__ head_w,
-    const int32_t* __restrict__ q_pos, int n_q, const int32_t* __restrict__ pool_in, int cand_blocks,
-    const uint8_t* __restrict__ idx_k, const uint8_t* __restrict__ idx_scale, const int32_t* __restrict__ n_entries,
-    float* __restrict__ scores, float* __restrict__ bmax, float* __restrict__ sbmax, int64_t dom_cap) {
-  scan_mfma_body<true>(ratio, capacity, idx_q, head_w, q_pos, n_q, pool_in, cand_blocks, idx_k, idx_scale, n_entries,
-                       scores, bmax, sbmax, dom_cap);
+// bf16: one super-block pair per batch, 2 waves per SIMD (the double load
+// buffer takes the registers of a third); FP4: one pair per batch at 3.
+template <bool POOL>
+__global__ __launch_bounds__(256, 2) void scan_mfma_bf16_kernel(SCAN_ARGS) {
+  scan_mfma_body<false, POOL, 1, kSbPerWave>(SCAN_PASS);
+}
+template <bool POOL>
+__global__ __launch_bounds__(256, 3) void scan_mfma_fp4_kernel(SCAN_ARGS) {
+  scan_mfma_body<true, POOL, 1, kSbPerWave>(SCAN_PASS);
 }
 
 // ------------------------------------------------------- query-blocked scan --
@@ -473,8 +540,11 @@ hipError_t launch_scan(const csa2_dims& dims, const csa2_kv_cache& cache, const 
   }
   if (mfma_shape) {
     const int64_t nsb = ss.dom_cap / 64;
+    if (nsb > (int64_t(1) << 24) || cache.capacity > (int64_t(1) << 24)) return hipErrorInvalidConfiguration;  // 32-bit slots
+    const bool fp4 = cache.kv_dtype == CSA2_FP4;
+    auto kern = fp4 ? (pool_in ? scan_mfma_fp4_kernel<true> : scan_mfma_fp4_kernel<false>)
+                    : (pool_in ? scan_mfma_bf16_kernel<true> : scan_mfma_bf16_kernel<false>);
     const dim3 grid(unsigned((nsb + 4 * kSbPerWave - 1) / (4 * kSbPerWave)), n_q, cache.batch);
-    auto kern = cache.kv_dtype == CSA2_FP4 ? scan_mfma_fp4_kernel : scan_mfma_bf16_kernel;
     const hipError_t err = launch_kernel(cache.kv_dtype == CSA2_FP4 ? CSA2_KERNEL_SCAN_FP4 : CSA2_KERNEL_SCAN_BF16, kern, grid, dim3(256), 0, stream, cache.ratio, cache.capacity,
                        static_cast<const uint16_t*>(idx_q), head_w, q_pos, n_q, pool_in, dims.cand_blocks,
                        static_cast<const uint8_t*>(cache.idx_k), cache.idx_scale, cache.n_entries, ss.scores, ss.bmax,
