@@ -75,8 +75,9 @@ __device__ __forceinline__ uint32_t waves_before(const SelLds L, int base, int w
 
 // Select the best min(m, #valid) of keys[0..n) (valid: key > kKeyNegInf),
 // ties to the lower position; write the chosen positions ascending to out[].
-// Returns the number chosen.  All threads of the block must call it; the
-// histograms are zero on entry and on exit.
+// Returns the number chosen.  All threads of the block must call it, after a
+// barrier that follows the put_stats() of the keys' writer; the histograms
+// are zero on entry and on exit.
 //
 // Thread t owns the run of R consecutive positions [R t, R t + R) (R a
 // multiple of 4, at most 16), read 16 bytes at a time.  The threshold key T
@@ -94,31 +95,6 @@ __device__ int select_top(const SelLds L, int n, int m, lds_u32* out) {
   const int p0 = R * tid;
   lds_u32* const hist = L.hist + kBins * (w & 3);
 
-  // count, min and max of the valid keys
-  uint32_t cnt = 0, kmn = 0xFFFFFFFFu, kmx = 0u;
-  for (int v = 0; v < R; v += 4) {
-    if (p0 + v >= n) break;
-    const u32x4 k4 = *reinterpret_cast<const lds_u32x4*>(L.keys + p0 + v);
-    const uint32_t kk[4] = {k4.x, k4.y, k4.z, k4.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t k = p0 + v + i < n ? kk[i] : kKeyNegInf;
-      if (k > kKeyNegInf) {
-        ++cnt;
-        kmn = min(kmn, k);
-        kmx = max(kmx, k);
-      }
-    }
-  }
-  cnt = __ockl_wfred_add_u32(cnt);
-  kmn = __ockl_wfred_min_u32(kmn);
-  kmx = __ockl_wfred_max_u32(kmx);
-  if (lane == 0) {
-    L.wred[w] = cnt;
-    L.wred[kNW + w] = kmn;
-    L.wred[2 * kNW + w] = kmx;
-  }
-  __syncthreads();
   const uint32_t total = reduce_waves(L, 0, 0);
   uint32_t lo = reduce_waves(L, kNW, 1), hi = reduce_waves(L, 2 * kNW, 2);
   __syncthreads();
@@ -192,7 +168,7 @@ __device__ int select_top(const SelLds L, int n, int m, lds_u32* out) {
   }
 
   // order-preserving compaction: (greater, equal) counts packed 16:16, one block scan
-  uint32_t gt = 0, eq = 0;
+  uint32_t gt = 0, eq = 0;  // T >= kKeyNegInf, so k > T implies a valid key
   for (int v = 0; v < R; v += 4) {
     if (p0 + v >= n) break;
     const u32x4 k4 = *reinterpret_cast<const lds_u32x4*>(L.keys + p0 + v);
@@ -200,7 +176,7 @@ __device__ int select_top(const SelLds L, int n, int m, lds_u32* out) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t k = p0 + v + i < n ? kk[i] : kKeyNegInf;
-      gt += k > T && k > kKeyNegInf;
+      gt += k > T;
       eq += k == T && k > kKeyNegInf;
     }
   }
@@ -222,14 +198,12 @@ __device__ int select_top(const SelLds L, int n, int m, lds_u32* out) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t k = p0 + v + i < n ? kk[i] : kKeyNegInf;
-      if (k <= kKeyNegInf) continue;
-      if (k > T) {
-        out[gt_run + min(eq_run, need)] = uint32_t(p0 + v + i);
-        ++gt_run;
-      } else if (k == T) {
-        if (eq_run < need) out[gt_run + eq_run] = uint32_t(p0 + v + i);
-        ++eq_run;
-      }
+      const bool g = k > T, e = k == T && k > kKeyNegInf;
+      // a greater key goes after the equal keys taken so far, an equal key
+      // is taken while fewer than `need` equal keys precede it
+      if (g || (e && eq_run < need)) out[gt_run + min(eq_run, need)] = uint32_t(p0 + v + i);
+      gt_run += g;
+      eq_run += e;
     }
   }
   __syncthreads();
@@ -242,14 +216,38 @@ __device__ __forceinline__ uint32_t key_in(const float* a, int64_t i, int64_t n)
   return (i >= 0 && i < n) ? score_key(a[i]) : kKeyNegInf;
 }
 
+// Count, min and max of the valid keys a thread wrote, summed over the block
+// into wred (per wave; select_top reduces the waves after the barrier).
+__device__ __forceinline__ void put_stats(const SelLds L, uint32_t cnt, uint32_t kmn, uint32_t kmx) {
+  cnt = __ockl_wfred_add_u32(cnt);
+  kmn = __ockl_wfred_min_u32(kmn);
+  kmx = __ockl_wfred_max_u32(kmx);
+  if ((threadIdx.x & 63) == 0) {
+    const int w = threadIdx.x >> 6;
+    L.wred[w] = cnt;
+    L.wred[kNW + w] = kmn;
+    L.wred[2 * kNW + w] = kmx;
+  }
+}
+
+__device__ __forceinline__ void note_key(uint32_t k, uint32_t& cnt, uint32_t& kmn, uint32_t& kmx) {
+  if (k > kKeyNegInf) {
+    ++cnt;
+    kmn = min(kmn, k);
+    kmx = max(kmx, k);
+  }
+}
+
 // keys[p] = key of src[idx(p)] for p in [0, cnt): kKeyForced where idx(p) is
-// `forced`, kKeyNegInf where idx(p) lies outside [0, n).  Each thread issues
-// kPer loads (at clamped, always valid addresses) before it uses any, so the
-// latencies of a batch overlap instead of adding up.  n >= 1.
+// `forced`, kKeyNegInf where idx(p) lies outside [0, n); then put_stats.
+// Each thread issues kPer loads (at clamped, always valid addresses) before
+// it uses any, so the latencies of a batch overlap instead of adding up.
+// n >= 1.
 template <class IdxFn>
-__device__ __forceinline__ void gather_keys(lds_u32* keys, int cnt, const float* __restrict__ src, int n,
-                                            int forced, IdxFn idx) {
+__device__ __forceinline__ void gather_keys(const SelLds L, int cnt, const float* __restrict__ src, int n, int forced,
+                                            IdxFn idx) {
   constexpr int kPer = 8;
+  uint32_t c = 0, kmn = 0xFFFFFFFFu, kmx = 0u;
   for (int base = 0; base < cnt; base += kPer * kNT) {
     int id[kPer];
     float v[kPer];
@@ -262,9 +260,14 @@ __device__ __forceinline__ void gather_keys(lds_u32* keys, int cnt, const float*
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int p = base + i * kNT + int(threadIdx.x);
-      if (p < cnt) keys[p] = id[i] == forced ? kKeyForced : ((id[i] >= 0 && id[i] < n) ? score_key(v[i]) : kKeyNegInf);
+      if (p < cnt) {
+        const uint32_t k = id[i] == forced ? kKeyForced : ((id[i] >= 0 && id[i] < n) ? score_key(v[i]) : kKeyNegInf);
+        L.keys[p] = k;
+        note_key(k, c, kmn, kmx);
+      }
     }
   }
+  put_stats(L, c, kmn, kmx);
 }
 
 __global__ __launch_bounds__(kNT) void select_kernel(int topk, int cand_blocks, int ratio, int64_t capacity,
@@ -302,18 +305,28 @@ __global__ __launch_bounds__(kNT) void select_kernel(int topk, int cand_blocks, 
     const int64_t n_vis = visible_count(n, q_pos[row], ratio);
     const int fb = n_vis > 0 ? int((n_vis - 1) / 8) : -1;
     const int fsb = fb >= 0 ? fb / 8 : -1;
+    const uint32_t fkey = fb >= 0 ? score_key(bm[fb]) : kKeyNegInf;  // the forced block's own key
     int na = nsb;
     if (nsb > cand_blocks) {
-      gather_keys(L.keys, nsb, sbm, nsb, fsb, [](int p) { return p; });
+      gather_keys(L, nsb, sbm, nsb, fsb, [](int p) { return p; });
       __syncthreads();
       na = select_top(L, nsb, cand_blocks, L.la);
     } else {
       for (int p = tid; p < nsb; p += kNT) L.la[p] = uint32_t(p);
       __syncthreads();  // la is read across threads below
     }
-    gather_keys(L.keys, 8 * na, bm, nb, fb, [&](int p) { return int(L.la[p >> 3]) * 8 + (p & 7); });
+    gather_keys(L, 8 * na, bm, nb, fb, [&](int p) { return int(L.la[p >> 3]) * 8 + (p & 7); });
     __syncthreads();
     const int npool = select_top(L, 8 * na, cand_blocks, L.lb);
+    // the pool members' own keys (the forced block's real maximum in place of
+    // its forced key), read before lb becomes block ids and keys is rewritten
+    uint32_t pk[kMaxList / kNT];
+#pragma unroll
+    for (int i = 0; i < kMaxList / kNT; ++i) {
+      const int x = tid + i * kNT;
+      pk[i] = x < npool ? L.keys[L.lb[x]] : kKeyNegInf;
+      if (pk[i] == kKeyForced) pk[i] = fkey;
+    }
     // pool block ids (ascending), in place: thread x reads and writes lb[x] only
     for (int x = tid; x < npool; x += kNT) L.lb[x] = min(L.la[L.lb[x] >> 3] * 8 + (L.lb[x] & 7), uint32_t(nb - 1));
     for (int x = tid; x < cand_blocks; x += kNT) pool_out[row * cand_blocks + x] = x < npool ? int32_t(L.lb[x]) : -1;
@@ -322,7 +335,16 @@ __global__ __launch_bounds__(kNT) void select_kernel(int topk, int cand_blocks, 
     // topk <= cand_blocks - 1: the pool holds the best cand_blocks - 1 blocks
     // other than the forced one.  So the top-k stage needs only the pool.
     if (topk < cand_blocks) {
-      gather_keys(L.keys, npool, bm, nb, -1, [&](int p) { return int(L.lb[p]); });
+      uint32_t c = 0, kmn = 0xFFFFFFFFu, kmx = 0u;
+#pragma unroll
+      for (int i = 0; i < kMaxList / kNT; ++i) {
+        const int x = tid + i * kNT;
+        if (x < npool) {
+          L.keys[x] = pk[i];
+          note_key(pk[i], c, kmn, kmx);
+        }
+      }
+      put_stats(L, c, kmn, kmx);
       __syncthreads();
       nbsel = select_top(L, npool, topk, L.la);
       uint32_t ids[kMaxList / kNT];
@@ -345,14 +367,14 @@ __global__ __launch_bounds__(kNT) void select_kernel(int topk, int cand_blocks, 
   if (nbsel < 0) {
     int na = nsb;
     if (nsb > topk) {
-      gather_keys(L.keys, nsb, sbm, nsb, -1, [](int p) { return p; });
+      gather_keys(L, nsb, sbm, nsb, -1, [](int p) { return p; });
       __syncthreads();
       na = select_top(L, nsb, topk, L.la);
     } else {
       for (int p = tid; p < nsb; p += kNT) L.la[p] = uint32_t(p);
       __syncthreads();  // la is read across threads below
     }
-    gather_keys(L.keys, 8 * na, bm, nb, -1, [&](int p) { return int(L.la[p >> 3]) * 8 + (p & 7); });
+    gather_keys(L, 8 * na, bm, nb, -1, [&](int p) { return int(L.la[p >> 3]) * 8 + (p & 7); });
     __syncthreads();
     nbsel = select_top(L, 8 * na, topk, L.lb);
     // block ids of the chosen blocks (ascending), in place
@@ -361,7 +383,7 @@ __global__ __launch_bounds__(kNT) void select_kernel(int topk, int cand_blocks, 
   }
 
   // ---- top-k entries inside the chosen blocks ----
-  gather_keys(L.keys, 8 * nbsel, sc, int(dom_cap), -1, [&](int p) { return int(L.lb[p >> 3]) * 8 + (p & 7); });
+  gather_keys(L, 8 * nbsel, sc, int(dom_cap), -1, [&](int p) { return int(L.lb[p >> 3]) * 8 + (p & 7); });
   __syncthreads();
   const int ne = select_top(L, 8 * nbsel, topk, L.la);
   for (int x = tid; x < topk; x += kNT) {
