@@ -123,6 +123,8 @@ SMALL = {
     "group_small": replace(WORKLOADS["group_256k"], name="group_small", batch=2, prior=20000, new=1),
     "fp4_small": replace(WORKLOADS["fp4_1m"], name="fp4_small", batch=2, prior=20000, new=1),
     "fp4_pages": replace(WORKLOADS["fp4_1m"], name="fp4_pages", batch=2, prior=5000, new=1, main_group=16),
+    # a pool level of 8752 block keys: the sampled first pass of the selection
+    "pool_mid": replace(WORKLOADS["fp4_1m"], name="pool_mid", batch=1, prior=70000, new=1),
     "prefill_small": replace(WORKLOADS["prefill_128k"], name="prefill_small", prior=4096, new=512, n_q=512),
     "multi_q_small": replace(WORKLOADS["decode_32k"], name="multi_q_small", batch=2, prior=2990, new=10, n_q=10),
 }
