@@ -130,7 +130,7 @@ def run_gpu(wl, steps: int, warmup: int, copies: int, use_graph: bool):
     for _ in range(copies - 1):
         c = runner.DeviceCache(wl, wl.capacity, "cuda")
         c.main.copy_(step.cache.main)
-        c.idx.copy_(step.cache.idx)
+        c.idx_store.copy_(step.cache.idx_store)
         if c.main_scale is not None:
             c.main_scale.copy_(step.cache.main_scale)
             c.idx_scale.copy_(step.cache.idx_scale)

@@ -100,11 +100,20 @@ typedef struct csa2_dims {
  * j < n_entries[b].
  *
  *  F32 / BF16:  main  [batch][capacity][d]      act-sized elements of kv_dtype
- *               idx_k [batch][capacity][d_idx]
+ *               idx_k tiled, rows of d_idx elements (below)
  *  FP4:         main  [batch][capacity][d/2]     bytes (E2M1 codes)
  *               main_scale [batch][capacity][d/main_group]     E4M3 bytes
- *               idx_k [batch][capacity][d_idx/2] bytes
+ *               idx_k tiled, rows of d_idx/2 bytes (E2M1 codes)
  *               idx_scale  [batch][capacity][d_idx/idx_group]  E4M3 bytes
+ *
+ * Indexer K tiles: with P = capacity rounded up to a multiple of 32 and RB
+ * the row's bytes (4 d_idx, 2 d_idx or d_idx/2), idx_k holds batch * P * RB
+ * bytes; sequence b starts at byte b * P * RB and its rows form tiles of 32
+ * (tile t = rows 32t .. 32t+31, 32 * RB bytes).  Inside a tile the rows'
+ * 16-byte chunks are transposed: bytes [16c, 16c + 16) of row 32t + r lie at
+ * tile byte (32c + r) * 16.  The indexer's matrix-core loads, one row per
+ * lane, are then contiguous across lanes.  Padding rows are never read for
+ * an entry.
  * All base pointers must be 16-byte aligned.
  */
 typedef struct csa2_kv_cache {

@@ -28,13 +28,17 @@ constexpr int kPre = 32;  // input channels of W_ik a thread loads per batch
 // groups start at multiples of it), so the group's largest magnitude comes
 // from a butterfly over those lanes, every lane derives the same scale code,
 // encodes its own value, and the even lane of each pair writes the byte.
-__device__ void store_row(const double* v, int n, int dtype, int group, void* base, uint8_t* scale_base, int64_t row) {
+// `tiled`: the row goes to indexer K tile storage at data row `drow`; the
+// FP4 scales always go row-major to row `row`.
+__device__ void store_row(const double* v, int n, int dtype, int group, void* base, uint8_t* scale_base, int64_t row,
+                          bool tiled, int64_t drow) {
   const int c = threadIdx.x;
   const bool on = c < n;
+  uint8_t* bytes = reinterpret_cast<uint8_t*>(base);
   if (dtype == CSA2_F32) {
-    if (on) reinterpret_cast<float*>(base)[row * n + c] = __double2float_rn(v[c]);
+    if (on) *reinterpret_cast<float*>(bytes + (tiled ? idx_byte(drow, 4 * n, 4 * c) : (row * n + c) * 4)) = __double2float_rn(v[c]);
   } else if (dtype == CSA2_BF16) {
-    if (on) reinterpret_cast<uint16_t*>(base)[row * n + c] = f64_to_bf16(v[c]);
+    if (on) *reinterpret_cast<uint16_t*>(bytes + (tiled ? idx_byte(drow, 2 * n, 2 * c) : (row * n + c) * 2)) = f64_to_bf16(v[c]);
   } else {
     const double x = on ? v[c] : 0.0;
     double amax = fabs(x);
@@ -43,7 +47,7 @@ __device__ void store_row(const double* v, int n, int dtype, int group, void* ba
     const double s = e4m3_to_f64(sc);
     const uint32_t code = s > 0.0 ? e2m1_code(x, s) : 0u;
     const uint32_t odd = uint32_t(__shfl_xor(int(code), 1));
-    if (on && (c & 1) == 0) reinterpret_cast<uint8_t*>(base)[row * (n / 2) + c / 2] = uint8_t(code | (odd << 4));
+    if (on && (c & 1) == 0) bytes[tiled ? idx_byte(drow, n / 2, c / 2) : row * (n / 2) + c / 2] = uint8_t(code | (odd << 4));
     if (on && c % group == 0) scale_base[row * (n / group) + c / group] = uint8_t(sc);
   }
 }
@@ -138,7 +142,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
   __syncthreads();
 
   // 3. main KV row
-  store_row(e, d, kv_dtype, main_group, main, main_scale, row);
+  store_row(e, d, kv_dtype, main_group, main, main_scale, row, false, row);
 
   // 4. indexer K = e_hat . W_ik, from the unrounded rotated entry, summed
   // over the input channels in order; the float64 partials of the parts are
@@ -166,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
     kap[tid] = s;
   }
   __syncthreads();
-  store_row(kap, d_idx, kv_dtype, idx_group, idx_k, idx_scale, row);
+  store_row(kap, d_idx, kv_dtype, idx_group, idx_k, idx_scale, row, true, int64_t(b) * idx_rows_padded(capacity) + j);
 }
 
 }  // namespace

@@ -180,6 +180,32 @@ __device__ __forceinline__ float act_load(const void* base, int64_t off, int act
                   : reinterpret_cast<const float*>(base)[off];
 }
 
+// Indexer K layout.  Each sequence's rows are padded to a multiple of 32 and
+// stored in tiles of 32 rows; inside a tile the rows' 16-byte chunks are
+// transposed: chunk c of row r lies at byte (32 c + r % 32) * 16 of tile
+// r / 32, so chunk c of the tile's 32 rows is 512 contiguous bytes.  A load in
+// the MFMA operand layout (one lane per row, 16 bytes each) is then one
+// contiguous run per 32 lanes.  FP4 scales stay row-major.
+__host__ __device__ constexpr int64_t idx_rows_padded(int64_t capacity) { return (capacity + 31) / 32 * 32; }
+
+// Byte x of indexer K row `row` (row counted over all sequences, each padded
+// to idx_rows_padded(capacity) rows; row_bytes a multiple of 16).
+__device__ __forceinline__ int64_t idx_byte(int64_t row, int row_bytes, int x) {
+  return (row >> 5) * (int64_t(row_bytes) << 5) + ((int64_t(x >> 4) << 5) + (row & 31)) * 16 + (x & 15);
+}
+
+// Element c of indexer K row `row` (tiled as above; FP4 scales of the same
+// entry at row-major row `srow`).
+__device__ __forceinline__ float idx_load(const void* data, const uint8_t* scale, int dtype, int64_t row, int64_t srow,
+                                          int width, int group, int c) {
+  const uint8_t* d = reinterpret_cast<const uint8_t*>(data);
+  if (dtype == 0) return *reinterpret_cast<const float*>(d + idx_byte(row, 4 * width, 4 * c));
+  if (dtype == 1) return bf16_to_f32(*reinterpret_cast<const uint16_t*>(d + idx_byte(row, 2 * width, 2 * c)));
+  const uint8_t byte = d[idx_byte(row, width / 2, c >> 1)];
+  const uint32_t code = (c & 1) ? (byte >> 4) : (byte & 0xF);
+  return e2m1_to_f32(code) * e4m3_to_f32(scale[srow * (width / group) + c / group]);
+}
+
 // Element c of cache row `row` (F32 = 0, BF16 = 1, FP4 = 2).
 __device__ __forceinline__ float cache_load(const void* data, const uint8_t* scale, int dtype, int64_t row,
                                             int width, int group, int c) {

@@ -51,11 +51,11 @@ __global__ __launch_bounds__(kThreads) void scan_generic_kernel(
 
   float s = -INFINITY;
   if (j >= 0) {
-    const int64_t crow = int64_t(b) * capacity + j;
+    const int64_t crow = int64_t(b) * idx_rows_padded(capacity) + j, srow = int64_t(b) * capacity + j;
     s = 0.0f;
     for (int h = 0; h < Hi; ++h) {
       float dot = 0.0f;
-      for (int e = 0; e < di; ++e) dot += qs[h * di + e] * cache_load(idx_k, idx_scale, kv_dtype, crow, di, idx_group, e);
+      for (int e = 0; e < di; ++e) dot += qs[h * di + e] * idx_load(idx_k, idx_scale, kv_dtype, crow, srow, di, idx_group, e);
       s += ws[h] * fmaxf(dot, 0.0f);
     }
   }
@@ -169,7 +169,7 @@ __device__ __forceinline__ void scan_mfma_body(
   const int n_vis = int(visible_count(clamp_entries(n_entries, b, capacity), q_pos[row], ratio));
   const int sb0 = int(blockIdx.x) * (4 * kSbW) + wave;
   // this sequence's rows (bf16: 256 bytes, FP4: 64 code bytes + 4 scale bytes)
-  const uint8_t* kseq = idx_k + int64_t(b) * capacity * (FP4 ? 64 : 256);
+  const uint8_t* kseq = idx_k + int64_t(b) * idx_rows_padded(capacity) * (FP4 ? 64 : 256);
   const uint8_t* sseq = FP4 ? idx_scale + int64_t(b) * capacity * 4 : nullptr;
   const int32_t* prow = POOL ? pool_in + row * cand_blocks : nullptr;
   float* srow = scores + row * dom_cap;
@@ -191,15 +191,15 @@ __device__ __forceinline__ void scan_mfma_body(
       B.valid[t] = sb < nsb && j >= 0 && j < n_vis;
       const int jj = B.valid[t] ? j : 0;
       if (any_visible) {
+        // tile jj / 32, row jj % 32: chunk c at (32 c + jj % 32) * 16
+        const uint8_t* tile = kseq + int64_t(jj >> 5) * (FP4 ? 2048 : 8192) + (jj & 31) * 16;
         if constexpr (FP4) {
-          const uint8_t* p = kseq + int64_t(jj) * 64 + 16 * h;
 #pragma unroll
-          for (int g2 = 0; g2 < 2; ++g2) B.kf[t][g2] = *reinterpret_cast<const uint4*>(p + 32 * g2);
+          for (int g2 = 0; g2 < 2; ++g2) B.kf[t][g2] = *reinterpret_cast<const uint4*>(tile + (2 * g2 + h) * 512);
           B.ks[t] = *reinterpret_cast<const uint32_t*>(sseq + int64_t(jj) * 4) >> (8 * h);
         } else {
-          const uint4* p = reinterpret_cast<const uint4*>(kseq + int64_t(jj) * 256 + 128 * h);
 #pragma unroll
-          for (int q = 0; q < 8; ++q) B.kb[t][q] = p[q];
+          for (int q = 0; q < 8; ++q) B.kb[t][q] = *reinterpret_cast<const uint4*>(tile + (8 * h + q) * 512);
         }
       }
     }
@@ -397,9 +397,10 @@ __global__ __launch_bounds__(256, 1) void scan_prefill_kernel(
   for (int blk = 0; blk < 4; ++blk) {
     int64_t e = e0 + 32 * blk + n;
     e = e < capacity ? e : capacity - 1;  // slots past the cache: any valid row (masked below)
-    const uint4* p = reinterpret_cast<const uint4*>(idx_k + ((int64_t(b) * capacity + e) * 128 + 8 * hl) * 2);
+    // tile e / 32 of this sequence, row e % 32: chunk c at (32 c + e % 32) * 16
+    const uint8_t* tile = idx_k + (int64_t(b) * idx_rows_padded(capacity) + (e & ~int64_t(31))) * 256 + (e & 31) * 16;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) kreg[blk][s] = p[2 * s];  // channels 16s + 8hl .. +8
+    for (int s = 0; s < 8; ++s) kreg[blk][s] = *reinterpret_cast<const uint4*>(tile + (2 * s + hl) * 512);  // channels 16s + 8hl .. +8
   }
   // copies of the query tiles of heads 2p and 2p+1 into stage p & 1: 16
   // instructions of 1 KB (4 query rows each); wave w issues 4 of them

@@ -28,32 +28,51 @@ def make_dims(wl) -> B.Dims:
                   act_dtype=_DT[wl.act], rope_theta=wl.rope_theta)
 
 
+def idx_padded_rows(capacity: int) -> int:
+    """Indexer K rows per sequence in the library's tile storage (32-row tiles)."""
+    return (capacity + 31) // 32 * 32
+
+
 class DeviceCache:
-    """Main KV + indexer K of ``batch`` sequences with ``capacity`` entry slots."""
+    """Main KV + indexer K of ``batch`` sequences with ``capacity`` entry slots.
+
+    The indexer K lives in the library's tile storage (``idx_store``: per
+    sequence, 32-row tiles whose 16-byte chunks are transposed); ``idx``
+    returns it as row-major rows ([batch][padded rows][...]) for inspection.
+    """
 
     def __init__(self, wl, capacity: int, device="cuda"):
         self.wl = wl
         self.capacity = capacity
         b, d, di = wl.batch, wl.d, wl.d_idx
         kv = wl.kv
+        rows = idx_padded_rows(capacity)
         if kv == "fp4":
             self.main = torch.zeros((b, capacity, d // 2), dtype=torch.uint8, device=device)
             self.main_scale = torch.zeros((b, capacity, d // wl.main_group), dtype=torch.uint8, device=device)
-            self.idx = torch.zeros((b, capacity, di // 2), dtype=torch.uint8, device=device)
+            self.idx_dtype, self.idx_row_bytes = torch.uint8, di // 2
             self.idx_scale = torch.zeros((b, capacity, di // wl.idx_group), dtype=torch.uint8, device=device)
         else:
             dt = torch.bfloat16 if kv == "bf16" else torch.float32
             self.main = torch.zeros((b, capacity, d), dtype=dt, device=device)
-            self.idx = torch.zeros((b, capacity, di), dtype=dt, device=device)
+            self.idx_dtype, self.idx_row_bytes = dt, di * (2 if kv == "bf16" else 4)
             self.main_scale = self.idx_scale = None
+        self.idx_store = torch.zeros((b, rows * self.idx_row_bytes), dtype=torch.uint8, device=device)
         self.n_entries = torch.zeros(b, dtype=torch.int32, device=device)
+
+    @property
+    def idx(self) -> torch.Tensor:
+        """The indexer K as row-major rows (a copy), [batch][padded rows][d_idx or d_idx/2]."""
+        b, rb = self.wl.batch, self.idx_row_bytes
+        t = self.idx_store.view(b, -1, rb // 16, 32, 16).permute(0, 1, 3, 2, 4).reshape(b, -1, rb)
+        return t.contiguous().view(self.idx_dtype)
 
     def struct(self, with_idx: bool = True) -> B.KVCache:
         wl = self.wl
         return B.KVCache(
             kv_dtype=_DT[wl.kv], ratio=wl.ratio, main_group=wl.main_group, idx_group=wl.idx_group, batch=wl.batch,
             reserved0=0, capacity=self.capacity, main=B.ptr(self.main), main_scale=B.ptr(self.main_scale),
-            idx_k=B.ptr(self.idx) if with_idx else None, idx_scale=B.ptr(self.idx_scale) if with_idx else None,
+            idx_k=B.ptr(self.idx_store) if with_idx else None, idx_scale=B.ptr(self.idx_scale) if with_idx else None,
             n_entries=B.ptr(self.n_entries),
         )
 
