@@ -326,10 +326,13 @@ __global__ __launch_bounds__(256, 3) void scan_mfma_fp4_kernel(SCAN_ARGS) {
 //
 // Many queries per sequence (chunked prefill): the score contraction is a
 // GEMM per head, S_h = Q_h . K^T, whose K operand is shared by all 32 heads.
-// A workgroup (4 waves) owns 32 queries of one sequence and 512 entries; wave
-// w owns entries [128w, 128w+128).  Each wave loads its entries' indexer K
+// A workgroup (4 waves) owns 32 queries of one sequence and 256 entries; wave
+// w owns entries [64w, 64w+64).  Each wave loads its entries' indexer K
 // once, in registers, as the A operand of v_mfma_f32_32x32x16_bf16 (lane =
-// entry, 8 channels per lane and k-step; 4 blocks of 32 entries x 8 k-steps),
+// entry, 8 channels per lane and k-step; 2 blocks of 32 entries x 8 k-steps),
+// which keeps every operand and accumulator in the 256 architected registers
+// (with 128 entries per wave part of K went to AGPRs and came back by a copy
+// before every product) and lets two workgroups share a compute unit,
 // so the products are logits^T[entry][query]: a lane then holds one query and
 // runs of 4 consecutive entries, which makes the head weight one value per
 // lane, the score stores 16 bytes wide and a block maximum one exchange.
@@ -350,7 +353,8 @@ __global__ __launch_bounds__(256, 3) void scan_mfma_fp4_kernel(SCAN_ARGS) {
 constexpr int kPQ = 32;               // queries per query block
 constexpr int kQB = 1;                // query blocks per workgroup, in turn, sharing its resident K
                                       // (more than one overflows the register file at this tile size)
-constexpr int kPE = 512;              // entries per workgroup
+constexpr int kEB = 2;                // 32-entry blocks per wave (its resident K: 32 kEB registers)
+constexpr int kPE = 4 * 32 * kEB;     // entries per workgroup
 constexpr int kQTile = kPQ * 256;     // one head's query rows (bytes)
 
 typedef float f32x16_t_ __attribute__((__vector_size__(64)));
@@ -367,7 +371,7 @@ __device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds_addr
 // LDS slot (16 bytes) of chunk c (0..15) of query row q (0..31) in a head tile.
 __device__ __forceinline__ int qslot(int q, int c) { return q * 16 + (c ^ (q & 15)); }
 
-__global__ __launch_bounds__(256, 1) void scan_prefill_kernel(
+__global__ __launch_bounds__(256, 2) void scan_prefill_kernel(
     int ratio, int64_t capacity, const uint16_t* __restrict__ idx_q, const float* __restrict__ head_w,
     const int32_t* __restrict__ q_pos, int n_q, const uint8_t* __restrict__ idx_k,
     const int32_t* __restrict__ n_entries, float* __restrict__ scores, float* __restrict__ bmax,
@@ -386,15 +390,15 @@ __global__ __launch_bounds__(256, 1) void scan_prefill_kernel(
   const int b = int(grp / nqs), qbase = int(grp % nqs) * (kQB * kPQ);
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 31, hl = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t e_wg = int64_t(eb) * kPE, e0 = e_wg + 128 * wave;
+  const int64_t e_wg = int64_t(eb) * kPE, e0 = e_wg + 32 * kEB * wave;
   const int64_t n_ent = clamp_entries(n_entries, b, capacity);
 
   // ---- issue first, independent of the bookkeeping below: this wave's
   // entries' indexer K (the A operand, resident for all heads) and the query
   // tiles of heads 0 and 1 ----
-  uint4 kreg[4][8];
+  uint4 kreg[kEB][8];
 #pragma unroll
-  for (int blk = 0; blk < 4; ++blk) {
+  for (int blk = 0; blk < kEB; ++blk) {
     int64_t e = e0 + 32 * blk + n;
     e = e < capacity ? e : capacity - 1;  // slots past the cache: any valid row (masked below)
     // tile e / 32 of this sequence, row e % 32: chunk c at (32 c + e % 32) * 16
@@ -446,20 +450,20 @@ __global__ __launch_bounds__(256, 1) void scan_prefill_kernel(
     const int64_t vmax = vis_max;
     const bool wave_live = e0 < vmax;  // some query sees some entry of this wave's range
 
-    f32x16_t_ sacc[4];
+    f32x16_t_ sacc[kEB];
 #pragma unroll
-    for (int blk = 0; blk < 4; ++blk) sacc[blk] = f32x16_t_{};
+    for (int blk = 0; blk < kEB; ++blk) sacc[blk] = f32x16_t_{};
 
     if (e_wg < vmax) {
       // logits of head hh from tile `qt` into acc
       auto contract = [&](const uint8_t* qt, f32x16_t_* acc) {
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) acc[blk] = f32x16_t_{};
+        for (int blk = 0; blk < kEB; ++blk) acc[blk] = f32x16_t_{};
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
           const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(qt + 16 * qslot(n, 2 * s + hl));
 #pragma unroll
-          for (int blk = 0; blk < 4; ++blk)
+          for (int blk = 0; blk < kEB; ++blk)
             acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[blk][s]), a, acc[blk], 0, 0, 0);
         }
       };
@@ -467,12 +471,12 @@ __global__ __launch_bounds__(256, 1) void scan_prefill_kernel(
       auto fold = [&](int hh, const f32x16_t_* acc) {
         const float w = wl[hh][n];
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk)
+        for (int blk = 0; blk < kEB; ++blk)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
             sacc[blk][r] += w * __int_as_float(max(__float_as_int(acc[blk][r]), 0));
       };
-      f32x16_t_ acc_a[4], acc_b[4];
+      f32x16_t_ acc_a[kEB], acc_b[kEB];
       for (int p = 0; p < 16; ++p) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies of heads 2p, 2p+1
         __syncthreads();  // every wave's copies landed; the other stage is free
@@ -494,9 +498,11 @@ __global__ __launch_bounds__(256, 1) void scan_prefill_kernel(
     const int64_t row = int64_t(b) * n_q + q;
     const int64_t vis = nvis[n];
     const int64_t nsb = dom_cap / 64;
-    float m_sb[2] = {-INFINITY, -INFINITY};
+    float m_sb[(kEB + 1) / 2];
 #pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
+    for (int i = 0; i < (kEB + 1) / 2; ++i) m_sb[i] = -INFINITY;
+#pragma unroll
+    for (int blk = 0; blk < kEB; ++blk) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int64_t e = e0 + 32 * blk + 8 * j + 4 * hl;
@@ -513,7 +519,7 @@ __global__ __launch_bounds__(256, 1) void scan_prefill_kernel(
       }
     }
 #pragma unroll
-    for (int p2 = 0; p2 < 2; ++p2) {
+    for (int p2 = 0; p2 < (kEB + 1) / 2; ++p2) {
       const int64_t sb = (e0 + 64 * p2) / 64;
       if (q < n_q && hl == 0 && sb < nsb) sbmax[row * nsb + sb] = m_sb[p2];
     }
