@@ -339,7 +339,7 @@ __global__ __launch_bounds__(256, 3) void scan_mfma_fp4_kernel(SCAN_ARGS) {
 // The heads then stream through LDS two at a time: the 32 queries' rows of
 // heads 2p and 2p+1 (2 x 8 KB) are copied global -> LDS (global_load_lds_dwordx4,
 // from inline assembly so the compiler does not drain them before LDS reads)
-// one pair ahead into a double buffer, and every wave contracts each head
+// two pairs ahead into three LDS stages, and every wave contracts each head
 // against its resident K (8 k-steps x 4 blocks), then adds w_h * max(0, logit)
 // into its 32 x 128 scores - one head's additions run under the next head's
 // products (two accumulator sets).  One workgroup barrier per head pair.  The
@@ -356,6 +356,7 @@ constexpr int kQB = 1;                // query blocks per workgroup, in turn, sh
 constexpr int kEB = 2;                // 32-entry blocks per wave (its resident K: 32 kEB registers)
 constexpr int kPE = 4 * 32 * kEB;     // entries per workgroup
 constexpr int kQTile = kPQ * 256;     // one head's query rows (bytes)
+constexpr int kStages = 3;            // head-pair stages in LDS (2..4): kStages - 1 pairs' copies fly
 
 typedef float f32x16_t_ __attribute__((__vector_size__(64)));
 
@@ -376,7 +377,7 @@ __global__ __launch_bounds__(256, 2) void scan_prefill_kernel(
     const int32_t* __restrict__ q_pos, int n_q, const uint8_t* __restrict__ idx_k,
     const int32_t* __restrict__ n_entries, float* __restrict__ scores, float* __restrict__ bmax,
     float* __restrict__ sbmax, int64_t dom_cap, int nqs, int neb, int groups) {
-  __shared__ __align__(16) uint8_t qtile[4][kQTile];  // 2 stages x 2 heads
+  __shared__ __align__(16) uint8_t qtile[2 * kStages][kQTile];  // kStages stages x 2 heads
   __shared__ __align__(16) float wl[32][kPQ];  // head weights [head][query]
   __shared__ int nvis[kPQ];
   __shared__ int vis_max;
@@ -410,7 +411,7 @@ __global__ __launch_bounds__(256, 2) void scan_prefill_kernel(
   // instructions of 1 KB (4 query rows each); wave w issues 4 of them
   auto issue_pair = [&](int p, int q0) {
     const uint32_t base = __builtin_amdgcn_readfirstlane(
-        uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)qtile[2 * (p & 1)])));
+        uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)qtile[2 * (p % kStages)])));
 #pragma unroll
     for (int m4 = 0; m4 < 4; ++m4) {
       const int m = 4 * wave + m4;          // 0..15: head 2p + m / 8, instruction m % 8
@@ -446,6 +447,7 @@ __global__ __launch_bounds__(256, 2) void scan_prefill_kernel(
     // every load so far (K included) complete, with a wait the compiler sees:
     // from here on the kernel's own vmcnt waits count only head copies
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    for (int pp = 1; pp < kStages - 1; ++pp) issue_pair(pp, q0);
     __syncthreads();
     const int64_t vmax = vis_max;
     const bool wave_live = e0 < vmax;  // some query sees some entry of this wave's range
@@ -478,11 +480,18 @@ __global__ __launch_bounds__(256, 2) void scan_prefill_kernel(
       };
       f32x16_t_ acc_a[kEB], acc_b[kEB];
       for (int p = 0; p < 16; ++p) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies of heads 2p, 2p+1
-        __syncthreads();  // every wave's copies landed; the other stage is free
-        if (p + 1 < 16) issue_pair(p + 1, q0);
+        // this wave's copies of heads 2p, 2p+1 landed; the copies of the
+        // pairs after p (at most kStages - 2, four instructions each) may fly
+        if (kStages == 4 && p < 14)
+          asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        else if (kStages >= 3 && p < 15)
+          asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();  // every wave's copies of pair p landed; pair p-1's stage is free
+        if (p + kStages - 1 < 16) issue_pair(p + kStages - 1, q0);
         if (!wave_live) continue;
-        const uint8_t* qt = qtile[2 * (p & 1)];
+        const uint8_t* qt = qtile[2 * (p % kStages)];
         contract(qt, acc_a);                       // head 2p
         if (p > 0) fold(2 * p - 1, acc_b);         // head 2p-1, under head 2p's products
         contract(qt + kQTile, acc_b);              // head 2p+1
