@@ -230,7 +230,12 @@ struct TileMask {
 };
 
 // FP4: the cache is FP4 with one E4M3 scale per MG channels (MG = 16 or 32).
-template <bool FP4, int MG>
+// SHARE (64 heads, many queries): one workgroup per query, wave w owns heads
+// 16w .. 16w+15, and the four waves run every row tile together from a
+// shared ring of two slabs, each wave copying (and for FP4 dequantising) four
+// of the tile's 16 rows: a row is gathered once per query instead of once per
+// head group.  No row splits, no cross-wave combine.
+template <bool FP4, int MG, bool SHARE>
 __global__ __launch_bounds__(256) void attn_mfma_kernel(
     int H, int topk, int window, int d_rope, int64_t capacity, RopeTable rope,
     const uint16_t* __restrict__ q, const int32_t* __restrict__ q_pos, int n_q, int64_t n_bq,
@@ -239,19 +244,29 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
     int tiles_per_split, int n_splits, uint16_t* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ part_o, float* __restrict__ part_ml) {
   extern __shared__ __align__(16) uint8_t lds[];
-  // workgroup -> (query, split, head group): the G head groups of one
-  // (query, split) pair share an XCD (id % 8), the pairs go round the XCDs
-  const int G = H / 16;
-  const int64_t wg = blockIdx.x, x8 = wg & 7, rest = wg >> 3;
-  const int hg = int(rest % G);
-  const int64_t pair = (rest / G) * 8 + x8;
-  if (pair >= n_bq * n_splits) return;  // padding workgroup (uniform)
-  const int64_t bq = pair / n_splits;
-  const int split = int(pair % n_splits);
-  const int64_t b = bq / n_q, t = q_pos[bq];
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  uint8_t* rs = lds + wave * 2 * kSlab;
+  const int64_t wg = blockIdx.x, x8 = wg & 7, rest = wg >> 3;
+  int hg, split;
+  int64_t bq;
+  if constexpr (SHARE) {
+    // workgroup -> query: consecutive queries (which share window rows) on one XCD
+    hg = wave;
+    split = 0;
+    bq = x8 * ((n_bq + 7) / 8) + rest;
+    if (bq >= n_bq) return;  // padding workgroup (uniform)
+  } else {
+    // workgroup -> (query, split, head group): the G head groups of one
+    // (query, split) pair share an XCD (id % 8), the pairs go round the XCDs
+    const int G = H / 16;
+    hg = int(rest % G);
+    const int64_t pair = (rest / G) * 8 + x8;
+    if (pair >= n_bq * n_splits) return;  // padding workgroup (uniform)
+    bq = pair / n_splits;
+    split = int(pair % n_splits);
+  }
+  const int64_t b = bq / n_q, t = q_pos[bq];
+  uint8_t* rs = SHARE ? lds : lds + wave * 2 * kSlab;
 
   const int tile_lo = split * tiles_per_split;
   const int tile_hi = min(n_tiles, tile_lo + tiles_per_split);
@@ -347,16 +362,19 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
     m.valid = uint32_t(__ballot(valid)) & 0xFFFFu;  // lanes 0..15 hold rows 0..15
     m.fp4 = uint32_t(__ballot(fp4)) & 0xFFFFu;
     if constexpr (FP4) {
-      const uint8_t* codes = main + crow * (kD / 2) + 64 * g;
+      if (!SHARE || (l16 >> 2) == wave) {  // SHARE: this wave's four rows
+        const uint8_t* codes = main + crow * (kD / 2) + 64 * g;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fr.c[i] = reinterpret_cast<const uint4*>(codes)[i];
-      fr.sc = *reinterpret_cast<const uint4*>(main_scale + crow * (kD / MG) + (MG == 16 ? 16 * (g >> 1) : 0));
+        for (int i = 0; i < 4; ++i) fr.c[i] = reinterpret_cast<const uint4*>(codes)[i];
+        fr.sc = *reinterpret_cast<const uint4*>(main_scale + crow * (kD / MG) + (MG == 16 ? 16 * (g >> 1) : 0));
+      }
     }
     const uint32_t slab = __builtin_amdgcn_readfirstlane(
         uint32_t(reinterpret_cast<uintptr_t>((lds_void*)(rs + buf * kSlab))));
     const uint64_t src_u = reinterpret_cast<uint64_t>(src);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int ii = 0; ii < (SHARE ? 4 : 16); ++ii) {
+      const int i = SHARE ? 4 * wave + ii : ii;  // uniform
       const uint64_t row = (uint64_t(uint32_t(__builtin_amdgcn_readlane(int(src_u >> 32), i))) << 32) |
                            uint32_t(__builtin_amdgcn_readlane(int(uint32_t(src_u)), i));
       copy_row_to_lds(reinterpret_cast<const void*>(row + 16 * lane), slab + i * kPitch);
@@ -375,7 +393,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
   auto dequant_tile = [&](int buf, const TileMask m, const Fp4Regs& fr) {
     uint8_t* slab = rs + buf * kSlab;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if ((m.fp4 >> l16) & 1u) {
+    if (((m.fp4 >> l16) & 1u) && (!SHARE || (l16 >> 2) == wave)) {
       const uint32_t w4[16] = {fr.c[0].x, fr.c[0].y, fr.c[0].z, fr.c[0].w, fr.c[1].x, fr.c[1].y,
                                fr.c[1].z, fr.c[1].w, fr.c[2].x, fr.c[2].y, fr.c[2].z, fr.c[2].w,
                                fr.c[3].x, fr.c[3].y, fr.c[3].z, fr.c[3].w};
@@ -405,7 +423,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
   // wait happened in dequant_tile).
   auto compute = [&](int buf, const TileMask m, bool more) {
     const uint8_t* slab = rs + buf * kSlab;
-    if constexpr (!FP4) {
+    if constexpr (!FP4 && !SHARE) {
       if (more) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
       else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
@@ -458,8 +476,43 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
   };
 
   Fp4Regs fa{}, fb{};
-  int tile = tile_lo + wave;
   TileMask ma{0u, 0u}, mb{0u, 0u};
+  if constexpr (SHARE) {
+    // every wave runs every tile; tile t is in slab t % 2 (a deeper ring of
+    // four slabs measured no faster: each wave's own latency chain, one wave
+    // per SIMD, bounds a tile, not the copies)
+    int tile = tile_lo;
+    if (tile < tile_hi) ma = issue(tile, 0, fa);
+    while (tile < tile_hi) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies and loads of `tile`
+      if constexpr (FP4) dequant_tile(0, ma, fa);
+      __syncthreads();  // the whole tile is in slab 0; every wave is done with slab 1
+      if (tile + 1 < tile_hi) mb = issue(tile + 1, 1, fb);
+      compute(0, ma, false);
+      if (++tile >= tile_hi) break;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if constexpr (FP4) dequant_tile(1, mb, fb);
+      __syncthreads();
+      if (tile + 1 < tile_hi) ma = issue(tile + 1, 0, fa);
+      compute(1, mb, false);
+      ++tile;
+    }
+    // each wave owns its heads: normalise and store, no combine
+    l_part += __shfl_xor(l_part, 16, kWave);
+    l_part += __shfl_xor(l_part, 32, kWave);
+    const float inv = l_part > 0.0f ? 1.0f / l_part : 0.0f;
+    const int64_t head = int64_t(wave) * 16 + l16;
+#pragma unroll
+    for (int cb = 0; cb < 32; ++cb) {
+      uint2 pk;
+      pk.x = uint32_t(f32_to_bf16(oacc[cb][0] * inv)) | (uint32_t(f32_to_bf16(oacc[cb][1] * inv)) << 16);
+      pk.y = uint32_t(f32_to_bf16(oacc[cb][2] * inv)) | (uint32_t(f32_to_bf16(oacc[cb][3] * inv)) << 16);
+      *reinterpret_cast<uint2*>(out + (bq * H + head) * kD + 16 * cb + 4 * g) = pk;
+    }
+    if (lse && g == 0) lse[bq * H + head] = l_part > 0.0f ? m_ref + logf(l_part) : -INFINITY;
+    return;
+  }
+  int tile = tile_lo + wave;
   if (tile < tile_hi) ma = issue(tile, 0, fa);
   while (tile < tile_hi) {
     const bool more_a = tile + 4 < tile_hi;
@@ -576,6 +629,7 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(int H, int n_splits, co
 
 struct AttnPlan {
   bool mfma;
+  bool share;  // one workgroup per query, waves = head groups (64 heads, many queries)
   int n_tiles, tiles_per_split, n_splits;
   int64_t n_blocks;  // 1-D grid of the MFMA kernel
 };
@@ -593,6 +647,11 @@ AttnPlan plan_attn(const csa2_dims& dims, const csa2_kv_cache& cache, int32_t n_
   p.n_splits = 1;
   if (!p.mfma || n_q <= 0) return p;
   const int64_t n_bq = int64_t(cache.batch) * n_q, G = dims.n_heads / 16;
+  if (dims.n_heads == 64 && n_bq >= 256) {  // enough queries to fill the chip one per workgroup
+    p.share = true;
+    p.n_blocks = 8 * ((n_bq + 7) / 8);
+    return p;
+  }
   const int64_t units = n_bq * G;
   int splits = int(units >= 256 ? 1 : (256 + units - 1) / units);
   splits = splits < 1 ? 1 : (splits > p.n_tiles ? p.n_tiles : splits);
@@ -628,16 +687,21 @@ hipError_t launch_attn(const csa2_dims& dims, const csa2_kv_cache& cache, const 
     if (p.n_blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     static bool attr_set = false;
     if (!attr_set) {
-      for (const void* f : {reinterpret_cast<const void*>(attn_mfma_kernel<false, 32>),
-                            reinterpret_cast<const void*>(attn_mfma_kernel<true, 32>),
-                            reinterpret_cast<const void*>(attn_mfma_kernel<true, 16>)}) {
+      for (const void* f : {reinterpret_cast<const void*>(attn_mfma_kernel<false, 32, false>),
+                            reinterpret_cast<const void*>(attn_mfma_kernel<true, 32, false>),
+                            reinterpret_cast<const void*>(attn_mfma_kernel<true, 16, false>),
+                            reinterpret_cast<const void*>(attn_mfma_kernel<false, 32, true>),
+                            reinterpret_cast<const void*>(attn_mfma_kernel<true, 32, true>),
+                            reinterpret_cast<const void*>(attn_mfma_kernel<true, 16, true>)}) {
         const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kAttnLds);
         if (e != hipSuccess) return e;
       }
       attr_set = true;
     }
-    auto kern = cache.kv_dtype != CSA2_FP4 ? attn_mfma_kernel<false, 32>
-                : (cache.main_group == 32 ? attn_mfma_kernel<true, 32> : attn_mfma_kernel<true, 16>);
+    auto kern = p.share ? (cache.kv_dtype != CSA2_FP4 ? attn_mfma_kernel<false, 32, true>
+                                 : (cache.main_group == 32 ? attn_mfma_kernel<true, 32, true> : attn_mfma_kernel<true, 16, true>))
+                        : (cache.kv_dtype != CSA2_FP4 ? attn_mfma_kernel<false, 32, false>
+                                 : (cache.main_group == 32 ? attn_mfma_kernel<true, 32, false> : attn_mfma_kernel<true, 16, false>));
     const int32_t kid = cache.kv_dtype != CSA2_FP4 ? CSA2_KERNEL_ATTN_BF16
                         : (cache.main_group == 32 ? CSA2_KERNEL_ATTN_FP4 : CSA2_KERNEL_ATTN_FP4_G16);
     hipError_t e = launch_kernel(kid, kern,

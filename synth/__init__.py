@@ -126,6 +126,8 @@ SMALL = {
     # a pool level of 8752 block keys: the sampled first pass of the selection
     "pool_mid": replace(WORKLOADS["fp4_1m"], name="pool_mid", batch=1, prior=70000, new=1),
     "prefill_small": replace(WORKLOADS["prefill_128k"], name="prefill_small", prior=4096, new=512, n_q=512),
+    "prefill_fp4_small": replace(WORKLOADS["prefill_128k"], name="prefill_fp4_small", kv="fp4", prior=4096, new=512,
+                                 n_q=512),
     "multi_q_small": replace(WORKLOADS["decode_32k"], name="multi_q_small", batch=2, prior=2990, new=10, n_q=10),
 }
 
