@@ -356,7 +356,9 @@ constexpr int kQB = 1;                // query blocks per workgroup, in turn, sh
 constexpr int kEB = 2;                // 32-entry blocks per wave (its resident K: 32 kEB registers)
 constexpr int kPE = 4 * 32 * kEB;     // entries per workgroup
 constexpr int kQTile = kPQ * 256;     // one head's query rows (bytes)
-constexpr int kStages = 3;            // head-pair stages in LDS (2..4): kStages - 1 pairs' copies fly
+constexpr int kHPS = 2;               // heads per LDS stage (even): one workgroup barrier per stage
+constexpr int kStages = 3;            // stages in LDS: kStages - 1 stages' copies fly
+constexpr int kNStage = 32 / kHPS;    // stages per query block
 
 typedef float f32x16_t_ __attribute__((__vector_size__(64)));
 
@@ -377,7 +379,7 @@ __global__ __launch_bounds__(256, 2) void scan_prefill_kernel(
     const int32_t* __restrict__ q_pos, int n_q, const uint8_t* __restrict__ idx_k,
     const int32_t* __restrict__ n_entries, float* __restrict__ scores, float* __restrict__ bmax,
     float* __restrict__ sbmax, int64_t dom_cap, int nqs, int neb, int groups) {
-  __shared__ __align__(16) uint8_t qtile[2 * kStages][kQTile];  // kStages stages x 2 heads
+  __shared__ __align__(16) uint8_t qtile[kHPS * kStages][kQTile];  // kStages stages x kHPS heads
   __shared__ __align__(16) float wl[32][kPQ];  // head weights [head][query]
   __shared__ int nvis[kPQ];
   __shared__ int vis_max;
@@ -407,15 +409,16 @@ __global__ __launch_bounds__(256, 2) void scan_prefill_kernel(
 #pragma unroll
     for (int s = 0; s < 8; ++s) kreg[blk][s] = *reinterpret_cast<const uint4*>(tile + (2 * s + hl) * 512);  // channels 16s + 8hl .. +8
   }
-  // copies of the query tiles of heads 2p and 2p+1 into stage p & 1: 16
-  // instructions of 1 KB (4 query rows each); wave w issues 4 of them
+  // copies of the query tiles of heads kHPS p .. kHPS p + kHPS - 1 into stage
+  // p % kStages: 8 kHPS instructions of 1 KB (4 query rows each); wave w
+  // issues 2 kHPS of them
   auto issue_pair = [&](int p, int q0) {
     const uint32_t base = __builtin_amdgcn_readfirstlane(
-        uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)qtile[2 * (p % kStages)])));
+        uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)qtile[kHPS * (p % kStages)])));
 #pragma unroll
-    for (int m4 = 0; m4 < 4; ++m4) {
-      const int m = 4 * wave + m4;          // 0..15: head 2p + m / 8, instruction m % 8
-      const int hh = 2 * p + (m >> 3);
+    for (int m4 = 0; m4 < 2 * kHPS; ++m4) {
+      const int m = 2 * kHPS * wave + m4;   // head kHPS p + m / 8, instruction m % 8
+      const int hh = kHPS * p + (m >> 3);
       const int slot = (m & 7) * 64 + lane;  // destination slot in that head's tile
       const int q = slot >> 4;               // query row of the slot
       const int c = (slot & 15) ^ (q & 15);  // its chunk (inverse of qslot)
@@ -479,23 +482,30 @@ __global__ __launch_bounds__(256, 2) void scan_prefill_kernel(
             sacc[blk][r] += w * __int_as_float(max(__float_as_int(acc[blk][r]), 0));
       };
       f32x16_t_ acc_a[kEB], acc_b[kEB];
-      for (int p = 0; p < 16; ++p) {
-        // this wave's copies of heads 2p, 2p+1 landed; the copies of the
-        // pairs after p (at most kStages - 2, four instructions each) may fly
-        if (kStages == 4 && p < 14)
+      for (int p = 0; p < kNStage; ++p) {
+        // this wave's copies of stage p landed; those of the stages after it
+        // (at most kStages - 2, 2 kHPS instructions each) may still fly
+        const int ahead = min(kStages - 2, kNStage - 1 - p) * 2 * kHPS;
+        if (ahead >= 16)
+          asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        else if (ahead >= 8)
           asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-        else if (kStages >= 3 && p < 15)
+        else if (ahead >= 4)
           asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
         else
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();  // every wave's copies of pair p landed; pair p-1's stage is free
-        if (p + kStages - 1 < 16) issue_pair(p + kStages - 1, q0);
+        __syncthreads();  // every wave's copies of stage p landed; stage p-1's slot is free
+        if (p + kStages - 1 < kNStage) issue_pair(p + kStages - 1, q0);
         if (!wave_live) continue;
-        const uint8_t* qt = qtile[2 * (p % kStages)];
-        contract(qt, acc_a);                       // head 2p
-        if (p > 0) fold(2 * p - 1, acc_b);         // head 2p-1, under head 2p's products
-        contract(qt + kQTile, acc_b);              // head 2p+1
-        fold(2 * p, acc_a);                        // head 2p, under head 2p+1's products
+        const uint8_t* qt = qtile[kHPS * (p % kStages)];
+#pragma unroll
+        for (int j = 0; j < kHPS; j += 2) {
+          const int h = kHPS * p + j;
+          contract(qt + j * kQTile, acc_a);               // head h
+          if (h > 0) fold(h - 1, acc_b);                  // head h-1, under head h's products
+          contract(qt + (j + 1) * kQTile, acc_b);         // head h+1
+          fold(h, acc_a);                                 // head h, under head h+1's products
+        }
       }
       if (wave_live) fold(31, acc_b);
     }
