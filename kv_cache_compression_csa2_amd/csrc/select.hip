@@ -50,7 +50,7 @@ struct SelLds {
   lds_u32* keys;  // [kMaxCand] candidate keys by position
   lds_u32* la;    // [kMaxList]
   lds_u32* lb;    // [kMaxList]
-  lds_u32* hist;  // [4 * kBins], four copies, all zero between passes
+  lds_u32* hist;  // [4 * kBins]: four copies, or one histogram of 4 kBins bins; all zero between passes
   lds_u32* wred;  // [4 * kNW] per-wave partial results
   lds_u32* misc;  // [8]
 };
@@ -82,18 +82,21 @@ __device__ __forceinline__ uint32_t waves_before(const SelLds L, int base, int w
 // Thread t owns the run of R consecutive positions [R t, R t + R) (R a
 // multiple of 4, at most 16), read 16 bytes at a time.  The threshold key T
 // is found by narrowing a key interval [lo, hi] that holds it: each pass
-// splits the interval into at most 2048 equal bins, and the interval shrinks
+// splits the interval into at most 2048 equal bins (8192 for 2049..4096 keys
+// of which at most a quarter are selected), and the interval shrinks
 // to the bin that holds the need-th largest key; when that bin is taken
 // whole the search stops early.  Starting from the observed [min, max] of the
 // keys spreads similar scores over many bins, and four copies of the
 // histogram (by wave) cut the LDS atomic collisions of clustered keys; three
 // passes always suffice for 32-bit keys.  The compaction is one block-wide
 // scan of packed (greater, equal) counts, then a short walk per thread.
-__device__ int select_top(const SelLds L, int n, int m, lds_u32* out) {
+template <bool FINE>
+__device__ int select_top_impl(const SelLds L, int n, int m, lds_u32* out) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int R = ((((n + kNT - 1) / kNT) + 3) & ~3);
   const int p0 = R * tid;
-  lds_u32* const hist = L.hist + kBins * (w & 3);
+  constexpr int bin_bits = FINE ? 13 : 11;
+  lds_u32* const hist = FINE ? L.hist : L.hist + kBins * (w & 3);
 
   const uint32_t total = reduce_waves(L, 0, 0);
   uint32_t lo = reduce_waves(L, kNW, 1), hi = reduce_waves(L, 2 * kNW, 2);
@@ -105,7 +108,7 @@ __device__ int select_top(const SelLds L, int n, int m, lds_u32* out) {
     for (;;) {
       const uint64_t width = uint64_t(hi) - lo + 1;
       const int bits = 64 - __clzll(width - 1);  // bits spanned by the interval
-      const int shift = bits > 11 ? bits - 11 : 0;
+      const int shift = bits > bin_bits ? bits - bin_bits : 0;
       for (int v = 0; v < R; v += 4) {
         if (p0 + v >= n) break;
         const u32x4 k4 = *reinterpret_cast<const lds_u32x4*>(L.keys + p0 + v);
@@ -117,17 +120,31 @@ __device__ int select_top(const SelLds L, int n, int m, lds_u32* out) {
         }
       }
       __syncthreads();
-      // bins [128w, 128w+128): lane holds bins b0 = 128w + 2*lane and b0 + 1 (four copies summed)
-      const int b0 = kBinsPerWave * w + 2 * lane;
-      uint32_t h0 = 0, h1 = 0;
+      // lane `lane` of wave w holds nb consecutive bins from b0 (fine: 8 of
+      // one histogram; else 2, four copies summed), read and zeroed
+      constexpr int nb = FINE ? 8 : 2;
+      const int b0 = FINE ? 8 * (64 * w + lane) : kBinsPerWave * w + 2 * lane;
+      uint32_t hb[nb];
+      if constexpr (FINE) {
+        lds_u32x4* hp = reinterpret_cast<lds_u32x4*>(L.hist + b0);
+        const u32x4 a = hp[0], c = hp[1];
+        hp[0] = u32x4{0u, 0u, 0u, 0u};
+        hp[1] = u32x4{0u, 0u, 0u, 0u};
+        hb[0] = a.x; hb[1] = a.y; hb[2] = a.z; hb[3] = a.w;
+        hb[4] = c.x; hb[5] = c.y; hb[6] = c.z; hb[7] = c.w;
+      } else {
+        hb[0] = hb[1] = 0u;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        h0 += L.hist[kBins * c + b0];
-        h1 += L.hist[kBins * c + b0 + 1];
-        L.hist[kBins * c + b0] = 0;
-        L.hist[kBins * c + b0 + 1] = 0;
+        for (int cp = 0; cp < 4; ++cp) {
+          hb[0] += L.hist[kBins * cp + b0];
+          hb[1] += L.hist[kBins * cp + b0 + 1];
+          L.hist[kBins * cp + b0] = 0;
+          L.hist[kBins * cp + b0 + 1] = 0;
+        }
       }
-      const uint32_t s = h0 + h1;
+      uint32_t s = 0;
+#pragma unroll
+      for (int i = 0; i < nb; ++i) s += hb[i];
       const uint32_t incl = __ockl_wfscan_add_u32(s, true);
       const uint32_t wtot = uint32_t(__builtin_amdgcn_readlane(int(incl), kWave - 1));
       if (lane == 0) L.wred[w] = wtot;
@@ -137,15 +154,15 @@ __device__ int select_top(const SelLds L, int n, int m, lds_u32* out) {
       const uint32_t incl_rev = __ockl_wfscan_add_u32(v, true);
       const uint32_t above_w = w == kNW - 1 ? 0u : uint32_t(__builtin_amdgcn_readlane(int(incl_rev), kNW - 2 - w));
       uint32_t above = above_w + (wtot - incl);
-      if (above < need && need <= above + s) {
-        if (need <= above + h1) {
-          L.misc[0] = uint32_t(b0 + 1);
-          L.misc[1] = need - above;
-          L.misc[2] = h1;
-        } else {
-          L.misc[0] = uint32_t(b0);
-          L.misc[1] = need - above - h1;
-          L.misc[2] = h0;
+      if (above < need && need <= above + s) {  // this lane holds the bin: walk its bins from the top
+#pragma unroll
+        for (int i = nb - 1; i >= 0; --i) {
+          if (need > above && need <= above + hb[i]) {
+            L.misc[0] = uint32_t(b0 + i);
+            L.misc[1] = need - above;
+            L.misc[2] = hb[i];
+          }
+          above += hb[i];
         }
       }
       __syncthreads();
@@ -208,6 +225,17 @@ __device__ int select_top(const SelLds L, int n, int m, lds_u32* out) {
   }
   __syncthreads();
   return int(chosen);
+}
+
+// 2049..4096 keys with at most a quarter selected: one histogram of
+// 4 kBins fine bins (few keys per bin in the upper tail, so the first pass
+// usually ends on a bin taken whole).  Otherwise four copies (by wave) of
+// kBins bins, which cut the atomic collisions of clustered keys; fine bins
+// measured slower there (a threshold in the dense middle, or 2048 clustered
+// pool maxima, still needs a second pass).
+__device__ int select_top(const SelLds L, int n, int m, lds_u32* out) {
+  if (n > 2048 && n <= 4096 && 4 * m <= n) return select_top_impl<true>(L, n, m, out);
+  return select_top_impl<false>(L, n, m, out);
 }
 
 // Key of a[i]; an index outside [0, n) (never produced by a correct
