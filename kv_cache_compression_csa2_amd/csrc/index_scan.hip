@@ -143,6 +143,33 @@ __device__ __forceinline__ uint32_t significand_pair(float s) {
 // max(x, 0) as an integer max on the bits (fmaxf adds a canonicalising max)
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
+// Signed-integer image of a float that orders like the float (negative
+// values have their magnitude bits flipped); its own inverse.  Maxima of
+// scores are taken on these, so each step is one integer max (a float max
+// would first canonicalise the exchanged operand).
+__device__ __forceinline__ int ord_int(int b) { return b ^ int(uint32_t(b >> 31) >> 1); }
+
+// Maximum with the value of another lane of the same 16-lane row, by DPP.
+template <int CTRL>
+__device__ __forceinline__ int max_dpp(int k) { return max(k, __builtin_amdgcn_mov_dpp(k, CTRL, 0xF, 0xF, false)); }
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141; // lane i of each 8 <- lane 7 - i
+constexpr int kDppMirror = 0x140;     // lane i of each 16 <- lane 15 - i
+
+// x of this lane plus x of the lane 32 away (the two halves swap through
+// v_permlane32_swap; whichever half each result holds, their sum is the pair's)
+__device__ __forceinline__ float add_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Maximum over the two 16-lane rows of each 32-lane half (rows 0 and 1, 2 and 3).
+__device__ __forceinline__ int max_row_pairs(int k) {
+  const auto r = __builtin_amdgcn_permlane16_swap(uint32_t(k), uint32_t(k), false, false);
+  return max(int(r[0]), int(r[1]));
+}
+
 // Tile loads of one batch (kBatch super-blocks = 2 kBatch tiles of 32 entries).
 template <bool FP4, int kBatch>
 struct ScanBatch {
@@ -258,7 +285,7 @@ __device__ __forceinline__ void scan_mfma_body(
     ScanBatch<FP4, kBatch>& B = buf[it & 1];
     const int sb_first = sb0 + 4 * kBatch * it;
     const bool any_visible = sb_first < nsb && (POOL || sb_first * 64 < n_vis);
-    float tmax[kTiles];
+    int tmax[kTiles];
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
       float part = 0.0f;
@@ -279,25 +306,33 @@ __device__ __forceinline__ void scan_mfma_body(
 #pragma unroll
           for (int q = 0; q < 8; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qop[q], as_bf16x8(B.kb[t][q]), acc, 0, 0, 0);
         }
+        // two partial sums: half the dependent chain
+        float part1 = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) part += wreg[r] * relu(acc[r]);
+        for (int r = 0; r < 16; r += 2) {
+          part = fmaf(wreg[r], relu(acc[r]), part);
+          part1 = fmaf(wreg[r + 1], relu(acc[r + 1]), part1);
+        }
+        part += part1;
       }
-      float sc = (part + __shfl_xor(part, 32, kWave)) * unscale;
+      // the entry's score: the lane's 16 heads plus the other half's 16
+      float sc = add_halves(part) * unscale;
       if (!B.valid[t]) sc = -INFINITY;
       const int sb = sb_first + 4 * (t >> 1);
       if (sb < nsb && h == 0) srow[B.slot[t]] = sc;
-      float m = fmaxf(sc, __shfl_xor(sc, 1, kWave));
-      m = fmaxf(m, __shfl_xor(m, 2, kWave));
-      m = fmaxf(m, __shfl_xor(m, 4, kWave));
-      if (sb < nsb && h == 0 && (n & 7) == 0) brow[B.slot[t] / 8] = m;
-      m = fmaxf(m, __shfl_xor(m, 8, kWave));
-      m = fmaxf(m, __shfl_xor(m, 16, kWave));
-      tmax[t] = m;
+      // block (8 lanes) and tile (32 lanes) maxima, as ordered integers
+      int m = ord_int(__float_as_int(sc));
+      m = max_dpp<kDppXor1>(m);
+      m = max_dpp<kDppXor2>(m);
+      m = max_dpp<kDppHalfMirror>(m);
+      if (sb < nsb && h == 0 && (n & 7) == 0) brow[B.slot[t] / 8] = __int_as_float(ord_int(m));
+      m = max_dpp<kDppMirror>(m);
+      tmax[t] = max_row_pairs(m);
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int sb = sb_first + 4 * u;
-      if (sb < nsb && lane == 0) sbrow[sb] = fmaxf(tmax[2 * u], tmax[2 * u + 1]);
+      if (sb < nsb && lane == 0) sbrow[sb] = __int_as_float(ord_int(max(tmax[2 * u], tmax[2 * u + 1])));
     }
   }
 }
