@@ -118,6 +118,7 @@ typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((__vector_size__(64)));
 
 constexpr int kSbPerWave = 4;
+constexpr int kFp4Ahead = 1;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
@@ -180,7 +181,7 @@ struct ScanBatch {
   uint32_t ks[FP4 ? 2 * kBatch : 1];
 };
 
-template <bool FP4, bool POOL, int kBatch, int kSbW>
+template <bool FP4, bool POOL, int kBatch, int kSbW, int kAhead>
 __device__ __forceinline__ void scan_mfma_body(
     int ratio, int64_t capacity, const uint16_t* __restrict__ idx_q, const float* __restrict__ head_w,
     const int32_t* __restrict__ q_pos, int n_q, const int32_t* __restrict__ pool_in, int cand_blocks,
@@ -232,8 +233,11 @@ __device__ __forceinline__ void scan_mfma_body(
     }
   };
 
-  ScanBatch<FP4, kBatch> buf[2];
-  issue(0, buf[0]);
+  // kAhead batches' loads fly while one is contracted
+  ScanBatch<FP4, kBatch> buf[kAhead + 1];
+#pragma unroll
+  for (int a = 0; a < kAhead; ++a)
+    if (a < kIters) issue(a, buf[a]);
 
   // A operand (indexer query) and the lane's 16 head weights, held for the whole scan
   const uint16_t* qrow = idx_q + (row * 32 + n) * 128;
@@ -281,37 +285,58 @@ __device__ __forceinline__ void scan_mfma_body(
 
 #pragma unroll
   for (int it = 0; it < kIters; ++it) {
-    if (it + 1 < kIters) issue(it + 1, buf[(it + 1) & 1]);
-    ScanBatch<FP4, kBatch>& B = buf[it & 1];
+    if (it + kAhead < kIters) issue(it + kAhead, buf[(it + kAhead) % (kAhead + 1)]);
+    ScanBatch<FP4, kBatch>& B = buf[it % (kAhead + 1)];
     const int sb_first = sb0 + 4 * kBatch * it;
     const bool any_visible = sb_first < nsb && (POOL || sb_first * 64 < n_vis);
     int tmax[kTiles];
+    // the tiles' products first, interleaved (independent accumulator
+    // chains keep the matrix pipe busy), then each tile's epilogue
+    f32x16_t acc[kTiles];
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) acc[t] = f32x16_t{};
+    if (any_visible) {
+      if constexpr (FP4) {
+        // this lane's groups: h (first 16 bytes) and 2 + h (second)
+        float sg[kTiles][2];
+        uint32_t mp[kTiles][2];
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) {
+          sg[t][0] = __builtin_amdgcn_cvt_f32_fp8(int(B.ks[t]), 0);
+          sg[t][1] = __builtin_amdgcn_cvt_f32_fp8(int(B.ks[t]), 2);
+          mp[t][0] = significand_pair(sg[t][0]);
+          mp[t][1] = significand_pair(sg[t][1]);
+        }
+#pragma unroll
+        for (int g2 = 0; g2 < 2; ++g2) {
+#pragma unroll
+          for (int sub = 0; sub < 4; ++sub) {
+#pragma unroll
+            for (int t = 0; t < kTiles; ++t) {
+              const uint32_t w4[4] = {B.kf[t][g2].x, B.kf[t][g2].y, B.kf[t][g2].z, B.kf[t][g2].w};
+              acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qop16[4 * g2 + sub], fp4x8_to_f16(w4[sub], sg[t][g2], mp[t][g2]),
+                                                              acc[t], 0, 0, 0);
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+          for (int t = 0; t < kTiles; ++t)
+            acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qop[q], as_bf16x8(B.kb[t][q]), acc[t], 0, 0, 0);
+      }
+    }
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
       float part = 0.0f;
       if (any_visible) {
-        f32x16_t acc = f32x16_t{};
-        if constexpr (FP4) {
-          // this lane's groups: h (first 16 bytes) and 2 + h (second)
-          const float sg[2] = {__builtin_amdgcn_cvt_f32_fp8(int(B.ks[t]), 0), __builtin_amdgcn_cvt_f32_fp8(int(B.ks[t]), 2)};
-#pragma unroll
-          for (int g2 = 0; g2 < 2; ++g2) {
-            const uint32_t mp = significand_pair(sg[g2]);
-            const uint32_t w4[4] = {B.kf[t][g2].x, B.kf[t][g2].y, B.kf[t][g2].z, B.kf[t][g2].w};
-#pragma unroll
-            for (int sub = 0; sub < 4; ++sub)
-              acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qop16[4 * g2 + sub], fp4x8_to_f16(w4[sub], sg[g2], mp), acc, 0, 0, 0);
-          }
-        } else {
-#pragma unroll
-          for (int q = 0; q < 8; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qop[q], as_bf16x8(B.kb[t][q]), acc, 0, 0, 0);
-        }
         // two partial sums: half the dependent chain
         float part1 = 0.0f;
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          part = fmaf(wreg[r], relu(acc[r]), part);
-          part1 = fmaf(wreg[r + 1], relu(acc[r + 1]), part1);
+          part = fmaf(wreg[r], relu(acc[t][r]), part);
+          part1 = fmaf(wreg[r + 1], relu(acc[t][r + 1]), part1);
         }
         part += part1;
       }
@@ -350,11 +375,11 @@ __device__ __forceinline__ void scan_mfma_body(
 // buffer takes the registers of a third); FP4: one pair per batch at 3.
 template <bool POOL>
 __global__ __launch_bounds__(256, 2) void scan_mfma_bf16_kernel(SCAN_ARGS) {
-  scan_mfma_body<false, POOL, 1, kSbPerWave>(SCAN_PASS);
+  scan_mfma_body<false, POOL, 1, kSbPerWave, 1>(SCAN_PASS);
 }
 template <bool POOL>
 __global__ __launch_bounds__(256, 3) void scan_mfma_fp4_kernel(SCAN_ARGS) {
-  scan_mfma_body<true, POOL, 1, kSbPerWave>(SCAN_PASS);
+  scan_mfma_body<true, POOL, 1, kSbPerWave, kFp4Ahead>(SCAN_PASS);
 }
 
 // ------------------------------------------------------- query-blocked scan --
