@@ -110,6 +110,17 @@ WORKLOADS = {
     ),
 }
 
+# The encoder macro-block: one Full layer that writes the cache and the
+# top-k, then five Reuse layers that attend with their own queries over the
+# same kept entries (zartbot walkthrough, section 2.3.3), on the chunked
+# prefill shape.
+ENCODER_BLOCK = (LayerPlan("full"),) + (LayerPlan("reuse", 0),) * 5
+WORKLOADS["encoder_block_128k"] = replace(
+    WORKLOADS["prefill_128k"], name="encoder_block_128k", layers=ENCODER_BLOCK,
+    description="encoder macro-block in chunked prefill, bf16: 131072 prior positions at ratio 2, a chunk of "
+    "4096 causal queries, 1 Full + 5 Reuse layers",
+)
+
 # Smaller cases of the same shapes, for parity at sizes the oracle finishes in seconds.
 SMALL = {
     "tiny_bf16": replace(WORKLOADS["tiny_encoder"], name="tiny_bf16", act="bf16", kv="bf16"),
@@ -129,6 +140,8 @@ SMALL = {
     "prefill_fp4_small": replace(WORKLOADS["prefill_128k"], name="prefill_fp4_small", kv="fp4", prior=4096, new=512,
                                  n_q=512),
     "multi_q_small": replace(WORKLOADS["decode_32k"], name="multi_q_small", batch=2, prior=2990, new=10, n_q=10),
+    "encoder_block_small": replace(WORKLOADS["prefill_128k"], name="encoder_block_small", prior=4096, new=512,
+                                   n_q=512, layers=ENCODER_BLOCK),
 }
 
 ALL = {**WORKLOADS, **SMALL}

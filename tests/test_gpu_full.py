@@ -23,6 +23,7 @@ FULL = {
     "group_256k": ([3], None),
     "fp4_1m": ([1], None),
     "prefill_128k": ([0], [0, 1, 777, 2048, 4095]),
+    "encoder_block_128k": ([0], [0, 2047, 4095]),
 }
 
 
