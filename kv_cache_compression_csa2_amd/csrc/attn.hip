@@ -174,6 +174,12 @@ constexpr int kLdsRope = kLdsMl + 2 * 4 * 16 * 4;                     // (cos, s
 constexpr int kLdsIds = kLdsRope + 2 * 64 * 4;                        // kept-entry ids of the workgroup's rows
 constexpr int kMaxIds = 2048 + 16;                                    // topk <= 2048, plus a straddling tile
 constexpr int kAttnLds = kLdsIds + kMaxIds * 4;
+// SHARE needs only its ring of two slabs, the rotation table and the ids, so
+// two workgroups fit a compute unit; with bf16 rows the kernel also fits the
+// registers of two waves per SIMD (FP4's dequantisation registers would spill)
+constexpr int kShareRope = 2 * kSlab;
+constexpr int kShareIds = kShareRope + 2 * 64 * 4;
+constexpr int kShareLds = kShareIds + kMaxIds * 4;
 // Softmax reference: logits are exponentiated against a per-head reference
 // max that is raised (and the output rescaled) only when a logit exceeds it
 // by more than this, so P stays below e^8 and the sums far from overflow.
@@ -236,7 +242,7 @@ struct TileMask {
 // of the tile's 16 rows: a row is gathered once per query instead of once per
 // head group.  No row splits, no cross-wave combine.
 template <bool FP4, int MG, bool SHARE>
-__global__ __launch_bounds__(256) void attn_mfma_kernel(
+__global__ __launch_bounds__(256, SHARE && !FP4 ? 2 : 1) void attn_mfma_kernel(
     int H, int topk, int window, int d_rope, int64_t capacity, RopeTable rope,
     const uint16_t* __restrict__ q, const int32_t* __restrict__ q_pos, int n_q, int64_t n_bq,
     const int32_t* __restrict__ topk_ids, const uint16_t* __restrict__ swa, const int32_t* __restrict__ swa_first,
@@ -276,7 +282,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
 
   // kept-entry ids of this workgroup's rows, and the rotation of this query's
   // position for each rotary pair, once per workgroup
-  int32_t* ids_lds = reinterpret_cast<int32_t*>(lds + kLdsIds);
+  int32_t* ids_lds = reinterpret_cast<int32_t*>(lds + (SHARE ? kShareIds : kLdsIds));
   const int row_lo = tile_lo * 16;
   {
     const int r_end = min(tile_hi * 16, topk);
@@ -292,7 +298,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
       if (r < r_end) ids_lds[r - row_lo] = idv[i];
     }
   }
-  float* rtab = reinterpret_cast<float*>(lds + kLdsRope);
+  float* rtab = reinterpret_cast<float*>(lds + (SHARE ? kShareRope : kLdsRope));
   if (tid < d_rope / 2) {
     const double phi = double(t) * rope.inv_freq[tid];
     const double two_pi = 6.283185307179586476925, inv_two_pi = 0.15915494309189533577;
@@ -705,7 +711,8 @@ hipError_t launch_attn(const csa2_dims& dims, const csa2_kv_cache& cache, const 
     const int32_t kid = cache.kv_dtype != CSA2_FP4 ? CSA2_KERNEL_ATTN_BF16
                         : (cache.main_group == 32 ? CSA2_KERNEL_ATTN_FP4 : CSA2_KERNEL_ATTN_FP4_G16);
     hipError_t e = launch_kernel(kid, kern,
-                                 dim3(unsigned(p.n_blocks)), dim3(256), kAttnLds, stream, dims.n_heads, dims.topk,
+                                 dim3(unsigned(p.n_blocks)), dim3(256), p.share ? kShareLds : kAttnLds, stream,
+                                 dims.n_heads, dims.topk,
                                  dims.window, dims.d_rope, cache.capacity, make_rope_table(dims),
                                  static_cast<const uint16_t*>(q), q_pos, n_q, int64_t(cache.batch) * n_q, topk,
                                  static_cast<const uint16_t*>(swa_kv), swa_first_pos, n_swa,
