@@ -121,10 +121,16 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
       for (int i = 0; i < ratio; ++i) mx = fmax(mx, double(pair_logits[i * d + c]));
       double den = 0.0;
       for (int i = 0; i < ratio; ++i) den += exp(double(pair_logits[i * d + c]) - mx);
-      for (int i = 0; i < ratio; ++i) {
+      // the weights sum to 1: the last row plus the weighted differences of
+      // the others (exact when the merged rows agree)
+      const int64_t row0 = (int64_t(b) * n_pos + int64_t(ratio) * m) * d + c;
+      const double last = double(act_load(latent, row0 + int64_t(ratio - 1) * d, act_bf16));
+      double dsum = 0.0;
+      for (int i = 0; i < ratio - 1; ++i) {
         const double a = exp(double(pair_logits[i * d + c]) - mx) / den;
-        acc += a * double(act_load(latent, (int64_t(b) * n_pos + int64_t(ratio) * m + i) * d + c, act_bf16));
+        dsum += a * (double(act_load(latent, row0 + int64_t(i) * d, act_bf16)) - last);
       }
+      acc = dsum + last;
     }
   }
 

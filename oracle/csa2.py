@@ -56,6 +56,11 @@ def compress(latent: np.ndarray, logits: np.ndarray | None, ratio: int) -> np.nd
     overlapping windows.  latent [T, d] with T a multiple of ratio ->
     entries [T/ratio, d]: e_j[c] = sum_i a[i, c] * X[ratio*j + i, c].
     Ratio 1 returns the latent unchanged.
+
+    The weights sum to 1, so the sum is evaluated as the last row plus the
+    weighted differences of the others from it: the same value, and exact
+    when the merged rows agree (a stored code then is that of the row itself,
+    also when the row sits on a rounding tie of the storage format).
     """
     x = np.asarray(latent, dtype=np.float64)
     t, d = x.shape
@@ -65,10 +70,11 @@ def compress(latent: np.ndarray, logits: np.ndarray | None, ratio: int) -> np.nd
         return x.copy()
     a = pair_weights(logits)
     groups = x.reshape(t // ratio, ratio, d)
+    last = groups[:, ratio - 1, :]
     out = np.zeros((t // ratio, d))
-    for i in range(ratio):
-        out += a[i][None, :] * groups[:, i, :]
-    return out
+    for i in range(ratio - 1):
+        out += a[i][None, :] * (groups[:, i, :] - last)
+    return out + last
 
 
 def entry_position(j: np.ndarray | int, ratio: int):

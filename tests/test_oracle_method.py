@@ -56,13 +56,24 @@ def test_compress_ratio1_is_identity():
 
 def test_compress_equal_logits_gives_mean_and_extremes_pick_one():
     rng = np.random.default_rng(1)
-    x = rng.standard_normal((12, 8))
+    # latent rows arrive in an activation type (float32 or bf16)
+    x = rng.standard_normal((12, 8)).astype(np.float32).astype(np.float64)
     e = csa2.compress(x, np.zeros((2, 8)), 2)
     assert np.allclose(e, (x[0::2] + x[1::2]) / 2, rtol=0, atol=1e-15)
     logits = np.zeros((2, 8))
     logits[0, :4], logits[1, 4:] = 800.0, 800.0  # channel-wise: first half picks row 0, rest row 1
     e = csa2.compress(x, logits, 2)
     assert np.array_equal(e[:, :4], x[0::2, :4]) and np.array_equal(e[:, 4:], x[1::2, 4:])
+
+
+def test_compress_of_equal_rows_is_that_row():
+    # a convex combination of equal rows is the row itself, exactly, whatever
+    # the weights: the stored code is then that of the row, ties included
+    rng = np.random.default_rng(3)
+    row = rng.standard_normal((5, 16)).astype(np.float32).astype(np.float64)
+    x = np.repeat(row, 2, axis=0)
+    for logits in (rng.standard_normal((2, 16)), np.zeros((2, 16)), 30 * rng.standard_normal((2, 16))):
+        assert np.array_equal(csa2.compress(x, logits, 2), row)
 
 
 def test_pair_weights_are_a_softmax_per_channel():
