@@ -82,7 +82,8 @@ def algorithmic_bytes(wl) -> dict:
     for p in wl.layers[1:]:
         if p.mode == "reindex":  # pool-domain rescoring: the pool's entries per query
             index += nq * (min(wl.cand_blocks * 8, wl.capacity) * idx_b + wl.n_idx_heads * (wl.d_idx * act + 4) + wl.topk * 4)
-    attn_one = nq * (wl.topk * (main_b + 4) + wl.window * wl.d * act + 2 * wl.n_heads * wl.d * act + wl.n_heads * 4)
+    swa_b = 1 if wl.swa == "fp8" else act  # window element: E4M3 byte or activation
+    attn_one = nq * (wl.topk * (main_b + 4) + wl.window * wl.d * swa_b + 2 * wl.n_heads * wl.d * act + wl.n_heads * 4)
     attn = attn_one * len(wl.layers)
     return {"compress": compress, "index": index, "attn": attn, "total": compress + index + attn}
 
@@ -289,7 +290,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.batch, "context": wl.context, "ratio": wl.ratio,
                    "kv": wl.kv, "heads": f"{wl.n_heads}x{wl.d}", "indexer": f"{wl.n_idx_heads}x{wl.d_idx}",
-                   "topk": wl.topk, "window": wl.window, "queries_per_seq": wl.n_q,
+                   "topk": wl.topk, "window": wl.window, "window_rows": "fp8" if wl.swa == "fp8" else wl.act,
+                   "queries_per_seq": wl.n_q,
                    "layers": [p.mode for p in wl.layers], "cache_copies": args.copies,
                    "launch": "eager" if args.eager else "hip_graph"},
         "step_hbm_gbps": round(nbytes["total"] / (ms * 1e-3) / 1e9, 1),

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 1
+#define CSA2_ABI_VERSION 2
 
 typedef enum csa2_status {
   CSA2_OK = 0,
@@ -60,8 +60,10 @@ typedef enum csa2_status {
 typedef enum csa2_dtype {
   CSA2_F32 = 0,  /* IEEE float32 */
   CSA2_BF16 = 1, /* bfloat16 bit patterns (uint16) */
-  CSA2_FP4 = 2   /* cache only: E2M1 codes, two per byte (even channel in the low
+  CSA2_FP4 = 2,  /* cache only: E2M1 codes, two per byte (even channel in the low
                     nibble), plus one E4M3 (FN) scale byte per group of channels */
+  CSA2_FP8 = 3   /* window rows only: one E4M3 (FN) byte per channel, no scale
+                    ([ZB] 2.4.4: the window KV stays in FP8) */
 } csa2_dtype;
 
 typedef enum csa2_mode {
@@ -90,6 +92,8 @@ typedef struct csa2_dims {
   int32_t cand_blocks; /* HSI pool size in blocks (2048); 1..2048 */
   int32_t act_dtype;   /* CSA2_F32 or CSA2_BF16 for latent, W_ik, q, idx_q, window rows, out */
   double rope_theta;   /* RoPE base (10000) */
+  int32_t swa_dtype;   /* window-row elements: 0 = act_dtype, or CSA2_FP8 */
+  int32_t reserved0;   /* must be 0 */
 } csa2_dims;
 
 /* The shared caches of one layer group: main KV and indexer K.
@@ -196,7 +200,8 @@ int csa2_index_topk(const csa2_dims* dims, const csa2_kv_cache* cache, const voi
  *  q             [batch][n_q][n_heads][d] act (not rotated)
  *  q_pos         [batch][n_q] int32
  *  topk          [batch][n_q][topk] int32 entry ids or -1
- *  swa_kv        [batch][n_swa][d] act, rows already rotated
+ *  swa_kv        [batch][n_swa][d] act (or E4M3 bytes if dims->swa_dtype is CSA2_FP8),
+ *                rows already rotated
  *  swa_first_pos [batch] int32: position of window-buffer row 0
  *  out           [batch][n_q][n_heads][d] act
  *  lse           NULL or [batch][n_q][n_heads] float32 (natural log)
@@ -219,7 +224,7 @@ typedef struct csa2_layer {
   const void* q;     /* [batch][n_q][n_heads][d] act */
   const void* idx_q; /* FULL/REINDEX: [batch][n_q][n_idx_heads][d_idx] act; REUSE: NULL */
   const float* head_w; /* FULL/REINDEX: [batch][n_q][n_idx_heads]; REUSE: NULL */
-  const void* swa_kv;  /* [batch][n_swa][d] act */
+  const void* swa_kv;  /* [batch][n_swa][d] act, or E4M3 bytes (dims->swa_dtype) */
   const int32_t* swa_first_pos; /* [batch] */
   void* out;         /* [batch][n_q][n_heads][d] act */
   float* lse;        /* NULL or [batch][n_q][n_heads] */

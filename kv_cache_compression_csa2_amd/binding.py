@@ -21,7 +21,7 @@ import torch  # noqa: F401  (must precede the CDLL below)
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libcsa2.so")
 
-F32, BF16, FP4 = 0, 1, 2
+F32, BF16, FP4, FP8 = 0, 1, 2, 3
 FULL, REINDEX, REUSE = 0, 1, 2
 EP_COMPRESS, EP_INDEX_TOPK, EP_SPARSE_ATTN, EP_LAYER_GROUP = 0, 1, 2, 3
 
@@ -36,7 +36,7 @@ class Dims(ctypes.Structure):
     _fields_ = [
         ("d", c_int32), ("d_rope", c_int32), ("n_heads", c_int32), ("n_idx_heads", c_int32), ("d_idx", c_int32),
         ("topk", c_int32), ("window", c_int32), ("block_size", c_int32), ("cand_blocks", c_int32),
-        ("act_dtype", c_int32), ("rope_theta", c_double),
+        ("act_dtype", c_int32), ("rope_theta", c_double), ("swa_dtype", c_int32), ("reserved0", c_int32),
     ]
 
 

@@ -54,6 +54,9 @@ int check_dims(const csa2_dims* d) {
   if (d->cand_blocks < 1 || d->cand_blocks > 2048) return fail(CSA2_ERR_UNSUPPORTED, "cand_blocks=%d: need 1..2048", d->cand_blocks);
   if (d->act_dtype != CSA2_F32 && d->act_dtype != CSA2_BF16) return fail(CSA2_ERR_UNSUPPORTED, "act_dtype=%d", d->act_dtype);
   if (!(d->rope_theta > 0.0)) return fail(CSA2_ERR_INVALID_ARG, "rope_theta must be positive");
+  if (d->swa_dtype != 0 && d->swa_dtype != CSA2_FP8)
+    return fail(CSA2_ERR_UNSUPPORTED, "swa_dtype=%d: need 0 (activation type) or CSA2_FP8", d->swa_dtype);
+  if (d->reserved0 != 0) return fail(CSA2_ERR_INVALID_ARG, "dims reserved field must be 0");
   return CSA2_OK;
 }
 

@@ -16,7 +16,7 @@ constexpr int kThreads = 256;
 
 // Generic path: one workgroup per (head, query, sequence), float32 math.
 __global__ __launch_bounds__(kThreads) void attn_generic_kernel(
-    int d, int d_rope, int H, int topk, int window, int act_bf16, int kv_dtype, int main_group, RopeTable rope,
+    int d, int d_rope, int H, int topk, int window, int act_bf16, int swa_fp8, int kv_dtype, int main_group, RopeTable rope,
     int64_t capacity, const void* __restrict__ q, const int32_t* __restrict__ q_pos, int n_q,
     const int32_t* __restrict__ topk_ids, const void* __restrict__ swa, const int32_t* __restrict__ swa_first,
     int n_swa, const void* __restrict__ main, const uint8_t* __restrict__ main_scale, void* __restrict__ out,
@@ -63,6 +63,11 @@ __global__ __launch_bounds__(kThreads) void attn_generic_kernel(
     }
   };
 
+  // window element: activation type, or one E4M3 (FN) byte
+  auto swa_load = [&](int64_t srow, int c) -> float {
+    return swa_fp8 ? e4m3_to_f32(static_cast<const uint8_t*>(swa)[srow * d + c]) : act_load(swa, srow * d + c, act_bf16);
+  };
+
   for (int r = wid; r < n_rows; r += kThreads / 64) {
     int64_t crow, srow;
     row_src(r, crow, srow);
@@ -70,8 +75,7 @@ __global__ __launch_bounds__(kThreads) void attn_generic_kernel(
     if (crow >= 0 || srow >= 0) {
       float part = 0.0f;
       for (int c = lane; c < d; c += 64) {
-        const float x = crow >= 0 ? cache_load(main, main_scale, kv_dtype, crow, d, main_group, c)
-                                  : act_load(swa, srow * d + c, act_bf16);
+        const float x = crow >= 0 ? cache_load(main, main_scale, kv_dtype, crow, d, main_group, c) : swa_load(srow, c);
         part += qh[c] * x;
       }
       v = wave_sum(part) * scale;
@@ -107,8 +111,7 @@ __global__ __launch_bounds__(kThreads) void attn_generic_kernel(
       if (p == 0.0f) continue;
       int64_t crow, srow;
       row_src(r, crow, srow);
-      const float x = crow >= 0 ? cache_load(main, main_scale, kv_dtype, crow, d, main_group, c)
-                                : act_load(swa, srow * d + c, act_bf16);
+      const float x = crow >= 0 ? cache_load(main, main_scale, kv_dtype, crow, d, main_group, c) : swa_load(srow, c);
       acc += p * x;
     }
     if (!(mx > -INFINITY)) acc = 0.0f;
@@ -233,6 +236,7 @@ struct Fp4Regs {
 struct TileMask {
   uint32_t valid;  // the row has a source
   uint32_t fp4;    // the row is an FP4 cache row
+  uint32_t w8;     // the row is an FP8 window row (copied as 512 bytes, widened in LDS)
 };
 
 // FP4: the cache is FP4 with one E4M3 scale per MG channels (MG = 16 or 32).
@@ -241,7 +245,9 @@ struct TileMask {
 // shared ring of two slabs, each wave copying (and for FP4 dequantising) four
 // of the tile's 16 rows: a row is gathered once per query instead of once per
 // head group.  No row splits, no cross-wave combine.
-template <bool FP4, int MG, bool SHARE>
+// W8: window rows are E4M3 (FN) bytes, copied as they are and widened to
+// bf16 in the slab (exact) before the tile is used.
+template <bool FP4, int MG, bool SHARE, bool W8>
 __global__ __launch_bounds__(256, SHARE && !FP4 ? 2 : 1) void attn_mfma_kernel(
     int H, int topk, int window, int d_rope, int64_t capacity, RopeTable rope,
     const uint16_t* __restrict__ q, const int32_t* __restrict__ q_pos, int n_q, int64_t n_bq,
@@ -361,12 +367,14 @@ __global__ __launch_bounds__(256, SHARE && !FP4 ? 2 : 1) void attn_mfma_kernel(
       const int64_t pp = win0 + (r - topk), sidx = pp - sfirst;
       if (swa && pp <= t && sidx >= 0 && sidx < n_swa) {
         valid = true;
-        src = reinterpret_cast<const uint8_t*>(swa + (b * n_swa + sidx) * kD);
+        src = W8 ? reinterpret_cast<const uint8_t*>(swa) + (b * n_swa + sidx) * kD
+                 : reinterpret_cast<const uint8_t*>(swa + (b * n_swa + sidx) * kD);
       }
     }
     TileMask m;
     m.valid = uint32_t(__ballot(valid)) & 0xFFFFu;  // lanes 0..15 hold rows 0..15
     m.fp4 = uint32_t(__ballot(fp4)) & 0xFFFFu;
+    m.w8 = W8 ? uint32_t(__ballot(valid && r >= topk)) & 0xFFFFu : 0u;
     if constexpr (FP4) {
       if (!SHARE || (l16 >> 2) == wave) {  // SHARE: this wave's four rows
         const uint8_t* codes = main + crow * (kD / 2) + 64 * g;
@@ -383,7 +391,10 @@ __global__ __launch_bounds__(256, SHARE && !FP4 ? 2 : 1) void attn_mfma_kernel(
       const int i = SHARE ? 4 * wave + ii : ii;  // uniform
       const uint64_t row = (uint64_t(uint32_t(__builtin_amdgcn_readlane(int(src_u >> 32), i))) << 32) |
                            uint32_t(__builtin_amdgcn_readlane(int(uint32_t(src_u)), i));
-      copy_row_to_lds(reinterpret_cast<const void*>(row + 16 * lane), slab + i * kPitch);
+      // an FP8 window row is 512 bytes: the upper half-wave copies it again
+      // into the slab row's upper half, which the widening overwrites
+      const uint32_t off = (W8 && (m.w8 >> i) & 1u) ? 16 * (lane & 31) : 16 * lane;
+      copy_row_to_lds(reinterpret_cast<const void*>(row + off), slab + i * kPitch);
     }
     return m;
   };
@@ -424,6 +435,30 @@ __global__ __launch_bounds__(256, SHARE && !FP4 ? 2 : 1) void attn_mfma_kernel(
     }
   };
 
+  // Widen the FP8 window rows this wave copied into slab `buf` (their copies
+  // have landed): one 8-byte read per lane takes the whole row before the
+  // 16-byte writes replace it with its bf16 values (E4M3 values are exact in
+  // bf16: at most 4 significant bits, exponents within range).
+  auto widen_w8 = [&](int buf, const TileMask m) {
+    uint8_t* slab = rs + buf * kSlab;
+#pragma unroll
+    for (int ii = 0; ii < (SHARE ? 4 : 16); ++ii) {
+      const int i = SHARE ? 4 * wave + ii : ii;  // uniform
+      if (!((m.w8 >> i) & 1u)) continue;
+      const uint2 v = *reinterpret_cast<const uint2*>(slab + i * kPitch + 8 * lane);
+      const uint32_t w2[2] = {v.x, v.y};
+      uint32_t o[4];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(w2[k]), false);  // bytes 0, 1
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(w2[k]), true);   // bytes 2, 3
+        o[2 * k] = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xFFFF0000u);
+        o[2 * k + 1] = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xFFFF0000u);
+      }
+      *reinterpret_cast<uint4*>(slab + i * kPitch + 16 * lane) = uint4{o[0], o[1], o[2], o[3]};
+    }
+  };
+
   // Compute the tile in slab `buf`.  `more`: the next tile's 16 copies were
   // issued after this tile's and may stay in flight (bf16 caches; for FP4 the
   // wait happened in dequant_tile).
@@ -433,6 +468,7 @@ __global__ __launch_bounds__(256, SHARE && !FP4 ? 2 : 1) void attn_mfma_kernel(
       if (more) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
       else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
+    if constexpr (W8 && !SHARE) widen_w8(buf, m);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     // ---- logits: lane holds head l16, rows 4g + r of the tile ----
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
@@ -482,7 +518,7 @@ __global__ __launch_bounds__(256, SHARE && !FP4 ? 2 : 1) void attn_mfma_kernel(
   };
 
   Fp4Regs fa{}, fb{};
-  TileMask ma{0u, 0u}, mb{0u, 0u};
+  TileMask ma{0u, 0u, 0u}, mb{0u, 0u, 0u};
   if constexpr (SHARE) {
     // every wave runs every tile; tile t is in slab t % 2 (a deeper ring of
     // four slabs measured no faster: each wave's own latency chain, one wave
@@ -492,12 +528,14 @@ __global__ __launch_bounds__(256, SHARE && !FP4 ? 2 : 1) void attn_mfma_kernel(
     while (tile < tile_hi) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies and loads of `tile`
       if constexpr (FP4) dequant_tile(0, ma, fa);
+      if constexpr (W8) widen_w8(0, ma);
       __syncthreads();  // the whole tile is in slab 0; every wave is done with slab 1
       if (tile + 1 < tile_hi) mb = issue(tile + 1, 1, fb);
       compute(0, ma, false);
       if (++tile >= tile_hi) break;
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       if constexpr (FP4) dequant_tile(1, mb, fb);
+      if constexpr (W8) widen_w8(1, mb);
       __syncthreads();
       if (tile + 1 < tile_hi) ma = issue(tile + 1, 0, fa);
       compute(1, mb, false);
@@ -693,21 +731,35 @@ hipError_t launch_attn(const csa2_dims& dims, const csa2_kv_cache& cache, const 
     if (p.n_blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     static bool attr_set = false;
     if (!attr_set) {
-      for (const void* f : {reinterpret_cast<const void*>(attn_mfma_kernel<false, 32, false>),
-                            reinterpret_cast<const void*>(attn_mfma_kernel<true, 32, false>),
-                            reinterpret_cast<const void*>(attn_mfma_kernel<true, 16, false>),
-                            reinterpret_cast<const void*>(attn_mfma_kernel<false, 32, true>),
-                            reinterpret_cast<const void*>(attn_mfma_kernel<true, 32, true>),
-                            reinterpret_cast<const void*>(attn_mfma_kernel<true, 16, true>)}) {
+      for (const void* f : {reinterpret_cast<const void*>(attn_mfma_kernel<false, 32, false, false>),
+                            reinterpret_cast<const void*>(attn_mfma_kernel<true, 32, false, false>),
+                            reinterpret_cast<const void*>(attn_mfma_kernel<true, 16, false, false>),
+                            reinterpret_cast<const void*>(attn_mfma_kernel<false, 32, true, false>),
+                            reinterpret_cast<const void*>(attn_mfma_kernel<true, 32, true, false>),
+                            reinterpret_cast<const void*>(attn_mfma_kernel<true, 16, true, false>),
+                            reinterpret_cast<const void*>(attn_mfma_kernel<false, 32, false, true>),
+                            reinterpret_cast<const void*>(attn_mfma_kernel<true, 32, false, true>),
+                            reinterpret_cast<const void*>(attn_mfma_kernel<true, 16, false, true>),
+                            reinterpret_cast<const void*>(attn_mfma_kernel<false, 32, true, true>),
+                            reinterpret_cast<const void*>(attn_mfma_kernel<true, 32, true, true>),
+                            reinterpret_cast<const void*>(attn_mfma_kernel<true, 16, true, true>)}) {
         const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kAttnLds);
         if (e != hipSuccess) return e;
       }
       attr_set = true;
     }
-    auto kern = p.share ? (cache.kv_dtype != CSA2_FP4 ? attn_mfma_kernel<false, 32, true>
-                                 : (cache.main_group == 32 ? attn_mfma_kernel<true, 32, true> : attn_mfma_kernel<true, 16, true>))
-                        : (cache.kv_dtype != CSA2_FP4 ? attn_mfma_kernel<false, 32, false>
-                                 : (cache.main_group == 32 ? attn_mfma_kernel<true, 32, false> : attn_mfma_kernel<true, 16, false>));
+    const bool w8 = dims.swa_dtype == CSA2_FP8;
+    auto pick = [&](auto k_bf16, auto k_fp4_32, auto k_fp4_16) {
+      return cache.kv_dtype != CSA2_FP4 ? k_bf16 : (cache.main_group == 32 ? k_fp4_32 : k_fp4_16);
+    };
+    auto kern = p.share ? (w8 ? pick(attn_mfma_kernel<false, 32, true, true>, attn_mfma_kernel<true, 32, true, true>,
+                                     attn_mfma_kernel<true, 16, true, true>)
+                              : pick(attn_mfma_kernel<false, 32, true, false>, attn_mfma_kernel<true, 32, true, false>,
+                                     attn_mfma_kernel<true, 16, true, false>))
+                        : (w8 ? pick(attn_mfma_kernel<false, 32, false, true>, attn_mfma_kernel<true, 32, false, true>,
+                                     attn_mfma_kernel<true, 16, false, true>)
+                              : pick(attn_mfma_kernel<false, 32, false, false>, attn_mfma_kernel<true, 32, false, false>,
+                                     attn_mfma_kernel<true, 16, false, false>));
     const int32_t kid = cache.kv_dtype != CSA2_FP4 ? CSA2_KERNEL_ATTN_BF16
                         : (cache.main_group == 32 ? CSA2_KERNEL_ATTN_FP4 : CSA2_KERNEL_ATTN_FP4_G16);
     hipError_t e = launch_kernel(kid, kern,
@@ -727,7 +779,7 @@ hipError_t launch_attn(const csa2_dims& dims, const csa2_kv_cache& cache, const 
   const dim3 grid(dims.n_heads, n_q, cache.batch);
   const size_t lds = sizeof(float) * size_t(dims.d + dims.topk + dims.window + kThreads / 64 + 2);
   const hipError_t err = launch_kernel(CSA2_KERNEL_ATTN_GENERIC, attn_generic_kernel, grid, dim3(kThreads), lds, stream, dims.d, dims.d_rope, dims.n_heads,
-                     dims.topk, dims.window, int(dims.act_dtype == CSA2_BF16), cache.kv_dtype, cache.main_group,
+                     dims.topk, dims.window, int(dims.act_dtype == CSA2_BF16), int(dims.swa_dtype == CSA2_FP8), cache.kv_dtype, cache.main_group,
                      make_rope_table(dims), cache.capacity, q, q_pos, n_q, topk, swa_kv, swa_first_pos, n_swa, cache.main,
                      cache.main_scale, out, lse);
   return err;

@@ -25,7 +25,8 @@ def act_tensor(x: np.ndarray, act: str, device) -> torch.Tensor:
 def make_dims(wl) -> B.Dims:
     return B.Dims(d=wl.d, d_rope=wl.d_rope, n_heads=wl.n_heads, n_idx_heads=wl.n_idx_heads, d_idx=wl.d_idx,
                   topk=wl.topk, window=wl.window, block_size=wl.block_size, cand_blocks=wl.cand_blocks,
-                  act_dtype=_DT[wl.act], rope_theta=wl.rope_theta)
+                  act_dtype=_DT[wl.act], rope_theta=wl.rope_theta, swa_dtype=B.FP8 if wl.swa == "fp8" else 0,
+                  reserved0=0)
 
 
 def idx_padded_rows(capacity: int) -> int:
@@ -101,7 +102,8 @@ class DeviceStep:
             swa, swa_first = inp.swa(li)
             L = dict(
                 plan=plan, q=act_tensor(inp.q(li), wl.act, device),
-                swa=act_tensor(swa, wl.act, device), swa_first=torch.from_numpy(swa_first).to(device),
+                swa=(torch.from_numpy(swa).to(device) if wl.swa == "fp8" else act_tensor(swa, wl.act, device)),
+                swa_first=torch.from_numpy(swa_first).to(device),
                 out=torch.empty((wl.batch, wl.n_q, wl.n_heads, wl.d), device=device,
                                 dtype=torch.bfloat16 if wl.act == "bf16" else torch.float32),
                 lse=torch.empty((wl.batch, wl.n_q, wl.n_heads), dtype=torch.float32, device=device),

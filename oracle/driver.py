@@ -15,7 +15,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import csa2
+from . import csa2, formats
 
 
 def dims_of(wl) -> csa2.Dims:
@@ -48,6 +48,8 @@ def layer_specs(inp, seqs) -> list:
     specs = []
     for li, plan in enumerate(wl.layers):
         swa, swa_first = inp.swa(li)
+        if wl.swa == "fp8":  # E4M3 (FN) bytes: the window KV kept in FP8 ([ZB] 2.4.4)
+            swa = formats.e4m3_decode(swa)
         specs.append(
             csa2.LayerSpec(
                 mode=plan.mode, source=plan.source, make_pool=plan.make_pool,

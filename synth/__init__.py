@@ -53,6 +53,7 @@ class Workload:
     main_group: int = 32
     idx_group: int = 32
     rope_theta: float = 10000.0
+    swa: str = "act"  # window-row storage: "act" (the activation dtype) or "fp8" (E4M3 bytes)
     description: str = ""
 
     @property
@@ -121,6 +122,15 @@ WORKLOADS["encoder_block_128k"] = replace(
     "4096 causal queries, 1 Full + 5 Reuse layers",
 )
 
+# The pages' storage format for the 1M decode: FP4 main KV with one E4M3 scale
+# per 16 channels (288 bytes per entry), FP4 indexer K with one per 32 (68
+# bytes), and the window KV kept in FP8 (zartbot walkthrough, section 2.4.4).
+WORKLOADS["fp4_1m_pages"] = replace(
+    WORKLOADS["fp4_1m"], name="fp4_1m_pages", main_group=16, swa="fp8",
+    description="long-context decode in the pages' storage format: 2 x 1048576, FP4 main KV per 16 channels, "
+    "FP4 indexer K per 32, FP8 (E4M3) window rows, HSI",
+)
+
 # Smaller cases of the same shapes, for parity at sizes the oracle finishes in seconds.
 SMALL = {
     "tiny_bf16": replace(WORKLOADS["tiny_encoder"], name="tiny_bf16", act="bf16", kv="bf16"),
@@ -142,6 +152,15 @@ SMALL = {
     "multi_q_small": replace(WORKLOADS["decode_32k"], name="multi_q_small", batch=2, prior=2990, new=10, n_q=10),
     "encoder_block_small": replace(WORKLOADS["prefill_128k"], name="encoder_block_small", prior=4096, new=512,
                                    n_q=512, layers=ENCODER_BLOCK),
+    # FP8 (E4M3) window rows on every attention path: float32 generic, bf16
+    # and FP4 caches, per-head-group and one-workgroup-per-query kernels
+    "tiny_fp8win": replace(WORKLOADS["tiny_encoder"], name="tiny_fp8win", swa="fp8"),
+    "decode_fp8win": replace(WORKLOADS["decode_32k"], name="decode_fp8win", batch=3, prior=3000, new=1, swa="fp8"),
+    "fp4_pages_fp8win": replace(WORKLOADS["fp4_1m_pages"], name="fp4_pages_fp8win", prior=5000, new=1),
+    "prefill_fp8win": replace(WORKLOADS["prefill_128k"], name="prefill_fp8win", prior=4096, new=512, n_q=512,
+                              swa="fp8"),
+    "prefill_fp4_fp8win": replace(WORKLOADS["prefill_128k"], name="prefill_fp4_fp8win", kv="fp4", prior=4096,
+                                  new=512, n_q=512, swa="fp8"),
 }
 
 ALL = {**WORKLOADS, **SMALL}
@@ -221,10 +240,23 @@ class Inputs:
         return self._normal((wl.batch, wl.n_q, wl.n_idx_heads), 1.0, "head_w", layer)
 
     def swa(self, layer: int) -> tuple[np.ndarray, np.ndarray]:
+        """Window rows and the position of row 0 per sequence.
+
+        FP8 windows are drawn directly as E4M3 (FN) code bytes: a random sign
+        and a magnitude code uniform over 0x20 .. 0x3F (0.125 .. 1.875, unit
+        scale like the N(0,1) rows), so the generator does no format
+        arithmetic; each side decodes the bytes.
+        """
         wl = self.wl
         first, n = wl.swa_span()
+        firsts = np.full(wl.batch, first, dtype=np.int32)
+        if wl.swa == "fp8":
+            rng = self._rng("swa", layer)
+            mag = rng.integers(0x20, 0x40, size=(wl.batch, n, wl.d), dtype=np.uint8)
+            sign = rng.integers(0, 2, size=(wl.batch, n, wl.d), dtype=np.uint8) << 7
+            return (mag | sign).astype(np.uint8), firsts
         rows = round_act(self._normal((wl.batch, n, wl.d), 1.0, "swa", layer), wl.act)
-        return rows, np.full(wl.batch, first, dtype=np.int32)
+        return rows, firsts
 
 
 def get(name: str) -> Workload:

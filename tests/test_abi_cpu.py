@@ -28,7 +28,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert B.csa2_abi_version() == 1
+    assert B.csa2_abi_version() == 2
     assert B.status_str(0) == "CSA2_OK"
     assert B.status_str(-4) == "CSA2_ERR_MODE_ORDER"
     assert B.status_str(-99) == "CSA2_ERR_UNKNOWN"
@@ -66,6 +66,8 @@ def call_index(d=None, c=None, ws=FAKE, ws_bytes=1 << 40, pool_in=None, pool_out
         (dict(cand_blocks=0), {}, -2),
         (dict(act_dtype=7), {}, -2),
         (dict(rope_theta=0.0), {}, -1),
+        (dict(swa_dtype=B.FP4), {}, -2),
+        (dict(reserved0=1), {}, -1),
         ({}, dict(ratio=3), -2),
         ({}, dict(kv_dtype=9), -2),
         ({}, dict(capacity=(1 << 20) + 1), -2),

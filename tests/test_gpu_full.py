@@ -24,6 +24,7 @@ FULL = {
     "fp4_1m": ([1], None),
     "prefill_128k": ([0], [0, 1, 777, 2048, 4095]),
     "encoder_block_128k": ([0], [0, 2047, 4095]),
+    "fp4_1m_pages": ([0], None),
 }
 
 
