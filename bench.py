@@ -71,7 +71,10 @@ def scan_work(wl) -> dict:
 
 def algorithmic_bytes(wl) -> dict:
     """Bytes the method must move per step, by stage (no scratch, no re-reads):
-    each sequence's indexer K is read once, each query gathers its kept rows."""
+    each sequence's indexer K is read once; a sequence's kept main-KV rows,
+    pool rows and window rows are counted once each (at most its n_q queries'
+    worth, at most the whole cache), its queries' own tensors once per query.
+    With one query per sequence (decode) every query's rows are its own."""
     act = 2 if wl.act == "bf16" else 4
     main_b = entry_bytes(wl.d, wl.kv, wl.main_group)
     idx_b = entry_bytes(wl.d_idx, wl.kv, wl.idx_group)
@@ -80,10 +83,14 @@ def algorithmic_bytes(wl) -> dict:
     compress = wl.batch * (wl.new * wl.d * act + n_new * (main_b + idx_b)) + wl.d * wl.d_idx * act
     index = scan_work(wl)["bytes"] + nq * wl.topk * 4
     for p in wl.layers[1:]:
-        if p.mode == "reindex":  # pool-domain rescoring: the pool's entries per query
-            index += nq * (min(wl.cand_blocks * 8, wl.capacity) * idx_b + wl.n_idx_heads * (wl.d_idx * act + 4) + wl.topk * 4)
+        if p.mode == "reindex":  # pool-domain rescoring: the pools' entries, the queries' indexer tensors
+            pool_rows = min(wl.n_q * min(wl.cand_blocks * 8, wl.capacity), wl.capacity)
+            index += wl.batch * pool_rows * idx_b + nq * (wl.n_idx_heads * (wl.d_idx * act + 4) + wl.topk * 4)
     swa_b = 1 if wl.swa == "fp8" else act  # window element: E4M3 byte or activation
-    attn_one = nq * (wl.topk * (main_b + 4) + wl.window * wl.d * swa_b + 2 * wl.n_heads * wl.d * act + wl.n_heads * 4)
+    kept_rows = min(wl.n_q * wl.topk, wl.capacity)
+    window_rows = wl.n_q + wl.window - 1
+    attn_one = (wl.batch * (kept_rows * main_b + window_rows * wl.d * swa_b)
+                + nq * (wl.topk * 4 + 2 * wl.n_heads * wl.d * act + wl.n_heads * 4))
     attn = attn_one * len(wl.layers)
     return {"compress": compress, "index": index, "attn": attn, "total": compress + index + attn}
 

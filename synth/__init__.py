@@ -131,6 +131,19 @@ WORKLOADS["fp4_1m_pages"] = replace(
     "FP4 indexer K per 32, FP8 (E4M3) window rows, HSI",
 )
 
+# Decoder-side chunked prefill: ratio 1, every query of the chunk builds its
+# own HSI pool in the Full layer and the Reindex layers rescore each query's
+# pool with their own indexer queries (zartbot walkthrough, sections 2.3.3
+# and 2.3.4: the decoder's first layer is Full and builds the candidate pool,
+# the following ones Reindex inside it).
+DECODER_PREFILL = (LayerPlan("full", make_pool=True), LayerPlan("reindex", 0), LayerPlan("reindex", 0))
+WORKLOADS["decoder_prefill_64k"] = replace(
+    WORKLOADS["decode_32k"], name="decoder_prefill_64k", batch=1, prior=65536, new=4096, n_q=4096,
+    layers=DECODER_PREFILL,
+    description="decoder chunked prefill, bf16: 65536 prior entries at ratio 1, a chunk of 4096 causal queries, "
+    "Full with per-query HSI pools + 2 Reindex layers",
+)
+
 # Smaller cases of the same shapes, for parity at sizes the oracle finishes in seconds.
 SMALL = {
     "tiny_bf16": replace(WORKLOADS["tiny_encoder"], name="tiny_bf16", act="bf16", kv="bf16"),
@@ -152,6 +165,8 @@ SMALL = {
     "multi_q_small": replace(WORKLOADS["decode_32k"], name="multi_q_small", batch=2, prior=2990, new=10, n_q=10),
     "encoder_block_small": replace(WORKLOADS["prefill_128k"], name="encoder_block_small", prior=4096, new=512,
                                    n_q=512, layers=ENCODER_BLOCK),
+    "decoder_prefill_small": replace(WORKLOADS["decoder_prefill_64k"], name="decoder_prefill_small", prior=8192,
+                                     new=256, n_q=256, cand_blocks=64, topk=128),
     # FP8 (E4M3) window rows on every attention path: float32 generic, bf16
     # and FP4 caches, per-head-group and one-workgroup-per-query kernels
     "tiny_fp8win": replace(WORKLOADS["tiny_encoder"], name="tiny_fp8win", swa="fp8"),

@@ -25,6 +25,7 @@ FULL = {
     "prefill_128k": ([0], [0, 1, 777, 2048, 4095]),
     "encoder_block_128k": ([0], [0, 2047, 4095]),
     "fp4_1m_pages": ([0], None),
+    "decoder_prefill_64k": ([0], [0, 2049, 4095]),
 }
 
 
