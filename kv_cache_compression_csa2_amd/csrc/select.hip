@@ -25,6 +25,8 @@
 // spread over 16 waves with short rolled loops, wave reductions and scans run
 // on DPP, and LDS is addressed through address-space-3 pointers so every
 // access is a ds_* instruction.
+#include <algorithm>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -233,7 +235,14 @@ __device__ int select_top_impl(const SelLds L, int n, int m, lds_u32* out) {
 // kBins bins, which cut the atomic collisions of clustered keys; fine bins
 // measured slower there (a threshold in the dense middle, or 2048 clustered
 // pool maxima, still needs a second pass).
-__device__ int select_top(const SelLds L, int n, int m, lds_u32* out) {
+__device__ __attribute__((noinline)) int select_top(const SelLds L, int n, int m, lds_u32* out) {
+  if (n > 2048 && n <= 4096 && 4 * m <= n) return select_top_impl<true>(L, n, m, out);
+  return select_top_impl<false>(L, n, m, out);
+}
+// The same, inlined: the 64-register variant of the kernel must not call a
+// function that allocates beyond that (the full variant keeps the call, whose
+// code measured ~2 us faster per pool selection)
+__device__ __forceinline__ int select_top_inl(const SelLds L, int n, int m, lds_u32* out) {
   if (n > 2048 && n <= 4096 && 4 * m <= n) return select_top_impl<true>(L, n, m, out);
   return select_top_impl<false>(L, n, m, out);
 }
@@ -271,10 +280,9 @@ __device__ __forceinline__ void note_key(uint32_t k, uint32_t& cnt, uint32_t& km
 // Each thread issues kPer loads (at clamped, always valid addresses) before
 // it uses any, so the latencies of a batch overlap instead of adding up.
 // n >= 1.
-template <class IdxFn>
+template <int kPer = 8, class IdxFn>
 __device__ __forceinline__ void gather_keys(const SelLds L, int cnt, const float* __restrict__ src, int n, int forced,
                                             IdxFn idx) {
-  constexpr int kPer = 8;
   uint32_t c = 0, kmn = 0xFFFFFFFFu, kmx = 0u;
   for (int base = 0; base < cnt; base += kPer * kNT) {
     int id[kPer];
@@ -298,7 +306,12 @@ __device__ __forceinline__ void gather_keys(const SelLds L, int cnt, const float
   put_stats(L, c, kmn, kmx);
 }
 
-__global__ __launch_bounds__(kNT) void select_kernel(int topk, int cand_blocks, int ratio, int64_t capacity,
+// KCAND: LDS key capacity of a level.  The full capacity (16384) leaves one
+// workgroup per compute unit; shapes whose levels gather at most 4096 keys
+// take a 66 KB variant bounded to 64 registers, so two workgroups share a
+// compute unit when many queries (chunked prefill) keep the chip busy.
+template <int KCAND>
+__device__ __forceinline__ void select_body(int topk, int cand_blocks, int ratio, int64_t capacity,
                                                      const int32_t* __restrict__ q_pos, int n_q,
                                                      const int32_t* __restrict__ pool_in,
                                                      const int32_t* __restrict__ n_entries,
@@ -308,13 +321,18 @@ __global__ __launch_bounds__(kNT) void select_kernel(int topk, int cand_blocks, 
                                                      float* __restrict__ topk_scores) {
   extern __shared__ uint32_t lds_raw[];
   lds_u32* lds = (lds_u32*)lds_raw;  // address-space cast into LDS
+  constexpr int kGather = KCAND <= 4096 ? 4 : 8;  // loads in flight per thread in a gather
   SelLds L;
   L.keys = lds;
-  L.la = L.keys + kMaxCand;
+  L.la = L.keys + KCAND;
   L.lb = L.la + kMaxList;
   L.hist = L.lb + kMaxList;
   L.wred = L.hist + 4 * kBins;
   L.misc = L.wred + 4 * kNW;
+  auto sel = [&](int n, int m, lds_u32* out) {
+    if constexpr (KCAND <= 4096) return select_top_inl(L, n, m, out);
+    else return select_top(L, n, m, out);
+  };
   for (int x = threadIdx.x; x < 4 * kBins; x += kNT) L.hist[x] = 0;
 
   const int qi = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
@@ -336,16 +354,16 @@ __global__ __launch_bounds__(kNT) void select_kernel(int topk, int cand_blocks, 
     const uint32_t fkey = fb >= 0 ? score_key(bm[fb]) : kKeyNegInf;  // the forced block's own key
     int na = nsb;
     if (nsb > cand_blocks) {
-      gather_keys(L, nsb, sbm, nsb, fsb, [](int p) { return p; });
+      gather_keys<kGather>(L, nsb, sbm, nsb, fsb, [](int p) { return p; });
       __syncthreads();
-      na = select_top(L, nsb, cand_blocks, L.la);
+      na = sel(nsb, cand_blocks, L.la);
     } else {
       for (int p = tid; p < nsb; p += kNT) L.la[p] = uint32_t(p);
       __syncthreads();  // la is read across threads below
     }
-    gather_keys(L, 8 * na, bm, nb, fb, [&](int p) { return int(L.la[p >> 3]) * 8 + (p & 7); });
+    gather_keys<kGather>(L, 8 * na, bm, nb, fb, [&](int p) { return int(L.la[p >> 3]) * 8 + (p & 7); });
     __syncthreads();
-    const int npool = select_top(L, 8 * na, cand_blocks, L.lb);
+    const int npool = sel(8 * na, cand_blocks, L.lb);
     // the pool members' own keys (the forced block's real maximum in place of
     // its forced key), read before lb becomes block ids and keys is rewritten
     uint32_t pk[kMaxList / kNT];
@@ -374,7 +392,7 @@ __global__ __launch_bounds__(kNT) void select_kernel(int topk, int cand_blocks, 
       }
       put_stats(L, c, kmn, kmx);
       __syncthreads();
-      nbsel = select_top(L, npool, topk, L.la);
+      nbsel = sel(npool, topk, L.la);
       uint32_t ids[kMaxList / kNT];
 #pragma unroll
       for (int i = 0; i < kMaxList / kNT; ++i) {
@@ -395,25 +413,25 @@ __global__ __launch_bounds__(kNT) void select_kernel(int topk, int cand_blocks, 
   if (nbsel < 0) {
     int na = nsb;
     if (nsb > topk) {
-      gather_keys(L, nsb, sbm, nsb, -1, [](int p) { return p; });
+      gather_keys<kGather>(L, nsb, sbm, nsb, -1, [](int p) { return p; });
       __syncthreads();
-      na = select_top(L, nsb, topk, L.la);
+      na = sel(nsb, topk, L.la);
     } else {
       for (int p = tid; p < nsb; p += kNT) L.la[p] = uint32_t(p);
       __syncthreads();  // la is read across threads below
     }
-    gather_keys(L, 8 * na, bm, nb, -1, [&](int p) { return int(L.la[p >> 3]) * 8 + (p & 7); });
+    gather_keys<kGather>(L, 8 * na, bm, nb, -1, [&](int p) { return int(L.la[p >> 3]) * 8 + (p & 7); });
     __syncthreads();
-    nbsel = select_top(L, 8 * na, topk, L.lb);
+    nbsel = sel(8 * na, topk, L.lb);
     // block ids of the chosen blocks (ascending), in place
     for (int x = tid; x < nbsel; x += kNT) L.lb[x] = L.la[L.lb[x] >> 3] * 8 + (L.lb[x] & 7);
     __syncthreads();
   }
 
   // ---- top-k entries inside the chosen blocks ----
-  gather_keys(L, 8 * nbsel, sc, int(dom_cap), -1, [&](int p) { return int(L.lb[p >> 3]) * 8 + (p & 7); });
+  gather_keys<kGather>(L, 8 * nbsel, sc, int(dom_cap), -1, [&](int p) { return int(L.lb[p >> 3]) * 8 + (p & 7); });
   __syncthreads();
-  const int ne = select_top(L, 8 * nbsel, topk, L.la);
+  const int ne = sel(8 * nbsel, topk, L.la);
   for (int x = tid; x < topk; x += kNT) {
     int32_t id = -1;
     float s = -INFINITY;
@@ -428,7 +446,23 @@ __global__ __launch_bounds__(kNT) void select_kernel(int topk, int cand_blocks, 
   }
 }
 
-constexpr size_t kSelectLds = sizeof(uint32_t) * (kMaxCand + 2 * kMaxList + 4 * kBins + 4 * kNW + 8);
+#define SELECT_ARGS                                                                                        \
+  int topk, int cand_blocks, int ratio, int64_t capacity, const int32_t *__restrict__ q_pos, int n_q,         \
+      const int32_t *__restrict__ pool_in, const int32_t *__restrict__ n_entries,                             \
+      const float *__restrict__ scores, const float *__restrict__ bmax, const float *__restrict__ sbmax,       \
+      int64_t dom_cap, int32_t *__restrict__ topk_out, int32_t *__restrict__ pool_out,                        \
+      float *__restrict__ topk_scores
+#define SELECT_PASS \
+  topk, cand_blocks, ratio, capacity, q_pos, n_q, pool_in, n_entries, scores, bmax, sbmax, dom_cap, topk_out, pool_out, topk_scores
+
+constexpr int kSmallCand = 4096;
+__global__ __launch_bounds__(kNT) void select_kernel(SELECT_ARGS) { select_body<kMaxCand>(SELECT_PASS); }
+// two workgroups per compute unit: 32 waves, at most 64 registers each
+__global__ __launch_bounds__(kNT) __attribute__((amdgpu_num_vgpr(64))) void select_kernel_wide(SELECT_ARGS) {
+  select_body<kSmallCand>(SELECT_PASS);
+}
+
+constexpr size_t select_lds(int kcand) { return sizeof(uint32_t) * (kcand + 2 * kMaxList + 4 * kBins + 4 * kNW + 8); }
 
 }  // namespace
 
@@ -438,11 +472,22 @@ hipError_t launch_select(const csa2_dims& dims, const csa2_kv_cache& cache, cons
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(select_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(kSelectLds));
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(select_lds(kMaxCand)));
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(select_kernel_wide),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, int(select_lds(kSmallCand)));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const hipError_t err = launch_kernel(CSA2_KERNEL_SELECT, select_kernel, dim3(n_q, cache.batch), dim3(kNT), kSelectLds, stream, dims.topk,
+  // keys each level gathers: super-block maxima (when they outnumber the
+  // level's m), then 8 per chosen super-block, then 8 per chosen block
+  const int64_t nsb = ss.dom_cap / 64;
+  const int64_t m_max = std::max<int64_t>(dims.topk, pool_out ? dims.cand_blocks : 0);
+  const int64_t most = std::max<int64_t>({nsb, 8 * std::min<int64_t>(nsb, m_max), 8 * int64_t(dims.topk)});
+  const bool small = most <= kSmallCand && int64_t(n_q) * cache.batch >= 512;
+  auto kern = small ? select_kernel_wide : select_kernel;
+  const hipError_t err = launch_kernel(CSA2_KERNEL_SELECT, kern, dim3(n_q, cache.batch), dim3(kNT),
+                                       select_lds(small ? kSmallCand : kMaxCand), stream, dims.topk,
                      dims.cand_blocks, cache.ratio, cache.capacity, q_pos, n_q, pool_in, cache.n_entries, ss.scores,
                      ss.bmax, ss.sbmax, ss.dom_cap, topk_out, pool_out, topk_scores);
   return err;
