@@ -1,0 +1,51 @@
+"""The benchmark's work accounting on the CPU: algorithmic bytes and flops of
+the measured workloads, worked out by hand from their shapes.
+
+decode_32k: 16 sequences x 32768 visible entries x 256 B of bf16 indexer K
+(134,217,728 B) + 16 x 32 x (128 x 2 + 4) B of indexer queries and head
+weights, the compress step (one 1024 B latent row in, a 1024 B main row and
+a 256 B indexer row out per sequence, W_ik 512 x 128 x 2 B once), 512 int32
+ids per query, and attention reading 512 kept rows (1024 B) + 128 window
+rows (1024 B) and the 64 x 512 bf16 query, writing the output and 64 float32
+log-sum-exps.
+"""
+import bench
+import synth
+
+
+def test_decode_32k_bytes():
+    wl = synth.get("decode_32k")
+    scan = 16 * 32768 * 256 + 16 * 32 * (128 * 2 + 4)
+    compress = 16 * (1024 + 1024 + 256) + 512 * 128 * 2
+    index = scan + 16 * 512 * 4
+    attn = 16 * (512 * 1024 + 128 * 1024) + 16 * (512 * 4 + 2 * 64 * 512 * 2 + 64 * 4)
+    got = bench.algorithmic_bytes(wl)
+    assert bench.scan_work(wl)["bytes"] == scan
+    assert (got["compress"], got["index"], got["attn"]) == (compress, index, attn)
+    assert got["total"] == 147_171_328
+
+
+def test_fp4_1m_bytes_and_scan_flops():
+    wl = synth.get("fp4_1m")
+    # FP4 indexer K: 64 code bytes + 4 scale bytes per entry; main KV 256 + 16
+    scan = 2 * 1048576 * 68 + 2 * 32 * (128 * 2 + 4)
+    assert bench.scan_work(wl)["bytes"] == scan
+    assert bench.scan_work(wl)["flops"] == 2 * 32 * 128 * 2 * 1048576
+    assert bench.algorithmic_bytes(wl)["total"] == 143_568_296
+
+
+def test_prefill_scan_flops_count_visible_pairs_only():
+    wl = synth.get("prefill_128k")
+    # query at 131072 + q sees 65536 + (q + 1) // 2 entries (ratio 2)
+    pairs = sum(65536 + (q + 1) // 2 for q in range(4096))
+    assert pairs == 272_629_760
+    assert bench.scan_work(wl)["flops"] == 2 * 32 * 128 * pairs
+
+
+def test_multi_query_rows_count_once():
+    wl = synth.get("prefill_128k")
+    # 4096 queries x 512 kept rows exceed the cache: each cached row once
+    one_layer = bench.algorithmic_bytes(wl)["attn"]
+    rows = 67584 * 1024 + (4096 + 127) * 1024
+    per_query = 4096 * (512 * 4 + 2 * 64 * 512 * 2 + 64 * 4)
+    assert one_layer == rows + per_query
