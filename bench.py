@@ -222,7 +222,7 @@ def cpu_baseline(wl, seconds: float) -> dict:
     while True:
         for i in range(len(seqs)):
             if wl.new:
-                oc.make_entries(new_lat[i], wl.prior, logits, w_ik, wl.ratio, wl.d_rope, wl.rope_theta, wl.kv,
+                oc.make_entries(new_lat[i], wl.prior, logits, w_ik, wl.ratio, wl.d_rope, driver.rope_cfg(wl), wl.kv,
                                 wl.main_group, wl.idx_group)
         oc.run_group(dims, caches, n_entries, q_pos, specs)
         done += len(seqs) * wl.n_q

@@ -93,7 +93,11 @@ typedef struct csa2_dims {
   int32_t act_dtype;   /* CSA2_F32 or CSA2_BF16 for latent, W_ik, q, idx_q, window rows, out */
   double rope_theta;   /* RoPE base (10000) */
   int32_t swa_dtype;   /* window-row elements: 0 = act_dtype, or CSA2_FP8 */
-  int32_t reserved0;   /* must be 0 */
+  int32_t rope_orig_len; /* YaRN: original context length (65536 in [ZB] 1.2); used when rope_factor > 1 */
+  double rope_factor;  /* YaRN context-extension factor s ([ZB] 1.2: 16); 0 or 1 = plain RoPE.  With s > 1
+                          rotary pair m turns at (1 - g) f_m / s + g f_m, f_m = theta^(-2m/d_rope),
+                          g = clamp((L f_m / (2 pi) - 1) / 31, 0, 1) with L = rope_orig_len, and the
+                          attention logits are scaled by (0.1 ln s + 1)^2 on top of 1/sqrt(d) */
 } csa2_dims;
 
 /* The shared caches of one layer group: main KV and indexer K.

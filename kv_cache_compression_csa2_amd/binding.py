@@ -36,7 +36,8 @@ class Dims(ctypes.Structure):
     _fields_ = [
         ("d", c_int32), ("d_rope", c_int32), ("n_heads", c_int32), ("n_idx_heads", c_int32), ("d_idx", c_int32),
         ("topk", c_int32), ("window", c_int32), ("block_size", c_int32), ("cand_blocks", c_int32),
-        ("act_dtype", c_int32), ("rope_theta", c_double), ("swa_dtype", c_int32), ("reserved0", c_int32),
+        ("act_dtype", c_int32), ("rope_theta", c_double), ("swa_dtype", c_int32), ("rope_orig_len", c_int32),
+        ("rope_factor", c_double),
     ]
 
 

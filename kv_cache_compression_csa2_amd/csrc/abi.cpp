@@ -56,7 +56,10 @@ int check_dims(const csa2_dims* d) {
   if (!(d->rope_theta > 0.0)) return fail(CSA2_ERR_INVALID_ARG, "rope_theta must be positive");
   if (d->swa_dtype != 0 && d->swa_dtype != CSA2_FP8)
     return fail(CSA2_ERR_UNSUPPORTED, "swa_dtype=%d: need 0 (activation type) or CSA2_FP8", d->swa_dtype);
-  if (d->reserved0 != 0) return fail(CSA2_ERR_INVALID_ARG, "dims reserved field must be 0");
+  if (!(d->rope_factor == 0.0 || d->rope_factor >= 1.0))
+    return fail(CSA2_ERR_INVALID_ARG, "rope_factor must be 0, 1 or more (YaRN factor)");
+  if (d->rope_factor > 1.0 && d->rope_orig_len <= 0)
+    return fail(CSA2_ERR_INVALID_ARG, "rope_orig_len must be positive with a YaRN factor above 1");
   return CSA2_OK;
 }
 

@@ -47,7 +47,7 @@ __global__ __launch_bounds__(kThreads) void attn_generic_kernel(
   const int64_t win0 = t - window + 1 > 0 ? t - window + 1 : 0;
   const int64_t sfirst = swa_first[b];
   const int n_rows = topk + window;
-  const float scale = 1.0f / sqrtf(float(d));
+  const float scale = rope.logit_scale;
 
   // row r < topk: main-KV entry topk_ids[r]; r >= topk: window position win0 + r - topk
   auto row_src = [&](int r, int64_t& crow, int64_t& srow) {
@@ -399,7 +399,7 @@ __global__ __launch_bounds__(256, SHARE && !FP4 ? 2 : 1) void attn_mfma_kernel(
     return m;
   };
 
-  const float scale = 0.044194173824159216f;  // 1/sqrt(512)
+  const float scale = rope.logit_scale;  // 1/sqrt(512), times the YaRN temperature
   float m_ref = -INFINITY, l_part = 0.0f;  // l_part: this lane's rows only
   f32x4 oacc[32];
 #pragma unroll

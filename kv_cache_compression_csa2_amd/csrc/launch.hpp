@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include "csa2.h"
@@ -17,12 +18,30 @@ namespace csa2 {
 // launch on the host (libm pow, float64) and passed by value to the kernels,
 // so no kernel evaluates a float64 pow per element.
 struct RopeTable {
-  double inv_freq[64];
+  double inv_freq[64];  // angle per position of each rotary pair
+  float logit_scale;    // attention logit scale: 1/sqrt(d), times the YaRN temperature
 };
 
+// Rotary frequencies theta^(-2m/d_rope); with a YaRN factor s > 1 (the
+// NTK-by-parts interpolation of the YaRN paper, Peng et al. 2023) a pair
+// whose wavelength fits the original context r = L f / (2 pi) times keeps
+// its frequency when r >= 32, is divided by s when r <= 1, and blends
+// linearly in between; the logits get the paper's temperature
+// (0.1 ln s + 1)^2.
 inline RopeTable make_rope_table(const csa2_dims& d) {
   RopeTable t{};
-  for (int m = 0; m < d.d_rope / 2 && m < 64; ++m) t.inv_freq[m] = std::pow(d.rope_theta, -2.0 * m / d.d_rope);
+  const bool yarn = d.rope_factor > 1.0;
+  for (int m = 0; m < d.d_rope / 2 && m < 64; ++m) {
+    double f = std::pow(d.rope_theta, -2.0 * m / d.d_rope);
+    if (yarn) {
+      const double r = double(d.rope_orig_len) * f / (2.0 * 3.14159265358979323846);
+      const double g = std::min(1.0, std::max(0.0, (r - 1.0) / 31.0));
+      f = (1.0 - g) * f / d.rope_factor + g * f;
+    }
+    t.inv_freq[m] = f;
+  }
+  const double ms = yarn ? 0.1 * std::log(d.rope_factor) + 1.0 : 1.0;
+  t.logit_scale = float(ms * ms / std::sqrt(double(d.d)));
   return t;
 }
 

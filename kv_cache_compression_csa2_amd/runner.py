@@ -26,7 +26,7 @@ def make_dims(wl) -> B.Dims:
     return B.Dims(d=wl.d, d_rope=wl.d_rope, n_heads=wl.n_heads, n_idx_heads=wl.n_idx_heads, d_idx=wl.d_idx,
                   topk=wl.topk, window=wl.window, block_size=wl.block_size, cand_blocks=wl.cand_blocks,
                   act_dtype=_DT[wl.act], rope_theta=wl.rope_theta, swa_dtype=B.FP8 if wl.swa == "fp8" else 0,
-                  reserved0=0)
+                  rope_orig_len=wl.rope_orig_len, rope_factor=wl.rope_factor)
 
 
 def idx_padded_rows(capacity: int) -> int:

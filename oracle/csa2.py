@@ -91,20 +91,59 @@ def entry_position(j: np.ndarray | int, ratio: int):
 # --------------------------------------------------------------------------
 
 
-def rope(x: np.ndarray, pos, d_rope: int, theta: float) -> np.ndarray:
+@dataclass(frozen=True)
+class Rope:
+    """RoPE settings: base theta, and the YaRN extension ([ZB] 1.2: original
+    length 65536, factor 16).  factor <= 1 is plain RoPE."""
+
+    theta: float = 10000.0
+    factor: float = 1.0
+    orig_len: int = 0
+
+
+def _rope_cfg(theta) -> Rope:
+    return theta if isinstance(theta, Rope) else Rope(float(theta))
+
+
+def rope_freqs(theta, d_rope: int) -> np.ndarray:
+    """Angle per position of rotary pair m = 0 .. d_rope/2 - 1.
+
+    Plain: f_m = theta^(-2m/d_rope).  YaRN (the pages name only its original
+    length and factor; the interpolation is the YaRN paper's "NTK-by-parts",
+    Peng et al. 2023, with its alpha = 1, beta = 32): with r_m the number of
+    wavelengths 2 pi / f_m that fit the original length L, a pair keeps f_m
+    when r_m >= 32, turns at f_m / s when r_m <= 1, and blends linearly in r
+    between the two.  **Parity unpinned by the pages** beyond factor and L.
+    """
+    cfg = _rope_cfg(theta)
+    m = np.arange(d_rope // 2, dtype=np.float64)
+    freq = np.power(float(cfg.theta), -2.0 * m / d_rope)
+    if cfg.factor > 1.0:
+        r = cfg.orig_len / (2.0 * np.pi / freq)
+        g = np.clip((r - 1.0) / (32.0 - 1.0), 0.0, 1.0)
+        freq = (1.0 - g) * (freq / cfg.factor) + g * freq
+    return freq
+
+
+def logit_temperature(theta) -> float:
+    """YaRN's attention temperature: logits times (0.1 ln s + 1)^2 (1 without YaRN)."""
+    cfg = _rope_cfg(theta)
+    return (0.1 * np.log(cfg.factor) + 1.0) ** 2 if cfg.factor > 1.0 else 1.0
+
+
+def rope(x: np.ndarray, pos, d_rope: int, theta) -> np.ndarray:
     """Rotate the trailing ``d_rope`` channels of ``x[..., d]`` by position ``pos``.
 
     [ZB] 1.2 lists 64 rotary dims inside the 512-d latent, theta 10000; the
     cache is stored after rotation ([ZB] 2.4.4).  Reading: the rotary channels
     are the last d_rope; pair m holds channels (c0 + 2m, c0 + 2m + 1) with
-    c0 = d - d_rope and turns by angle pos * theta^(-2m/d_rope).
-    ``pos`` broadcasts against x[..., 0].
+    c0 = d - d_rope and turns by angle pos * f_m (rope_freqs; ``theta`` is a
+    base or a Rope).  ``pos`` broadcasts against x[..., 0].
     """
     x = np.asarray(x, dtype=np.float64)
     d = x.shape[-1]
     c0 = d - d_rope
-    m = np.arange(d_rope // 2, dtype=np.float64)
-    freq = np.power(float(theta), -2.0 * m / d_rope)
+    freq = rope_freqs(theta, d_rope)
     phi = np.asarray(pos, dtype=np.float64)[..., None] * freq
     cos, sin = np.cos(phi), np.sin(phi)
     out = x.copy()
@@ -308,14 +347,16 @@ def pool_domain(pool: np.ndarray, beta: int, n_vis: int) -> np.ndarray:
 # --------------------------------------------------------------------------
 
 
-def attention(q: np.ndarray, t: int, rows: np.ndarray, d_rope: int, theta: float):
+def attention(q: np.ndarray, t: int, rows: np.ndarray, d_rope: int, theta):
     """Softmax attention of all heads of one query over the concatenated rows.
 
     [ZB] 2.2.2: global KV (sparse) and local KV (window) are concatenated and
     scored together with Q; [ZB] 3.3.1: key equals value, so the output is a
     convex combination of the rows.  Readings: the query is rotated at its
     own position t, logits are scaled by 1/sqrt(d), one softmax runs over all
-    rows (no de-duplication, no sink), and V is the full stored row.
+    rows (no de-duplication, no sink), and V is the full stored row.  With
+    YaRN (``theta`` a Rope with factor > 1) the logits also take its
+    temperature (logit_temperature).
     q [H, d], rows [n, d] -> (O [H, d], P [H, n], lse [H]) with lse the natural
     log of the softmax denominator of the scaled logits.
     """
@@ -324,7 +365,7 @@ def attention(q: np.ndarray, t: int, rows: np.ndarray, d_rope: int, theta: float
     rows = np.asarray(rows, dtype=np.float64)
     if rows.shape[0] == 0:
         raise ValueError("attention: no rows to attend to")
-    logits = (q_hat @ rows.T) / np.sqrt(d)
+    logits = (q_hat @ rows.T) * (logit_temperature(theta) / np.sqrt(d))
     m = logits.max(axis=1, keepdims=True)
     e = np.exp(logits - m)
     den = e.sum(axis=1, keepdims=True)
@@ -363,7 +404,7 @@ class Dims:
     block_size: int = 8
     cand_blocks: int = 2048
     ratio: int = 1
-    rope_theta: float = 10000.0
+    rope_theta: "float | Rope" = 10000.0  # a base, or a Rope with YaRN settings
 
 
 def full_scores(cache: "SeqCache", n_vis: int, q_idx, head_w, chunk: int = 1 << 16) -> np.ndarray:

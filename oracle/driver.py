@@ -18,11 +18,16 @@ import numpy as np
 from . import csa2, formats
 
 
+def rope_cfg(wl) -> csa2.Rope:
+    """RoPE settings of a workload (base theta, YaRN factor and original length)."""
+    return csa2.Rope(float(wl.rope_theta), float(wl.rope_factor), int(wl.rope_orig_len))
+
+
 def dims_of(wl) -> csa2.Dims:
     return csa2.Dims(
         d=wl.d, d_rope=wl.d_rope, n_heads=wl.n_heads, n_idx_heads=wl.n_idx_heads, d_idx=wl.d_idx,
         topk=wl.topk, window=wl.window, block_size=wl.block_size, cand_blocks=wl.cand_blocks,
-        ratio=wl.ratio, rope_theta=wl.rope_theta,
+        ratio=wl.ratio, rope_theta=rope_cfg(wl),
     )
 
 
@@ -35,7 +40,7 @@ def build_cache(inp, b: int, stop_pos: int, chunk: int = 1 << 14) -> csa2.SeqCac
     for p0 in range(0, stop_pos, chunk):
         p1 = min(stop_pos, p0 + chunk)
         _, main_raw, _, idx_raw, _ = csa2.make_entries(
-            inp.latent(b, p0, p1), p0, logits, w_ik, wl.ratio, wl.d_rope, wl.rope_theta, wl.kv,
+            inp.latent(b, p0, p1), p0, logits, w_ik, wl.ratio, wl.d_rope, rope_cfg(wl), wl.kv,
             wl.main_group, wl.idx_group,
         )
         cache.append(main_raw, idx_raw)
@@ -83,7 +88,7 @@ def run_step(inp, seqs=None, caches=None):
         if wl.new:
             _, main_raw, _, idx_raw, _ = csa2.make_entries(
                 inp.latent(b, wl.prior, wl.context), wl.prior, inp.pair_logits(), inp.w_ik(), wl.ratio,
-                wl.d_rope, wl.rope_theta, wl.kv, wl.main_group, wl.idx_group,
+                wl.d_rope, rope_cfg(wl), wl.kv, wl.main_group, wl.idx_group,
             )
             cache.append(main_raw, idx_raw)
         out_caches.append(cache)
@@ -112,7 +117,7 @@ class LazyMainCache(csa2.SeqCache):
             p1 = min(stop_pos, p0 + chunk)
             e = csa2.compress(inp.latent(b, p0, p1), logits, wl.ratio)
             j = p0 // wl.ratio + np.arange(e.shape[0])
-            e_hat = csa2.rope(e, csa2.entry_position(j, wl.ratio), wl.d_rope, wl.rope_theta)
+            e_hat = csa2.rope(e, csa2.entry_position(j, wl.ratio), wl.d_rope, rope_cfg(wl))
             _, idx_raw = formats_store(e_hat @ np.asarray(w_ik, dtype=np.float64), wl.kv, wl.idx_group)
             for key, arr in idx_raw.items():
                 self.idx_raw.setdefault(key, []).append(arr)
@@ -135,7 +140,7 @@ class LazyMainCache(csa2.SeqCache):
             for j in np.unique(sel):
                 q0 = int(j) * wl.ratio - p0
                 e = csa2.compress(lat[q0 : q0 + wl.ratio], self.inp.pair_logits(), wl.ratio)
-                e_hat = csa2.rope(e, csa2.entry_position(np.array([j]), wl.ratio), wl.d_rope, wl.rope_theta)
+                e_hat = csa2.rope(e, csa2.entry_position(np.array([j]), wl.ratio), wl.d_rope, rope_cfg(wl))
                 rows[int(j)] = formats_store(e_hat, wl.kv, wl.main_group)[1]
         keys = rows[int(ids[0])].keys() if len(ids) else []
         return {k: np.concatenate([rows[int(j)][k] for j in ids]) for k in keys}

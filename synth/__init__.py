@@ -53,6 +53,8 @@ class Workload:
     main_group: int = 32
     idx_group: int = 32
     rope_theta: float = 10000.0
+    rope_factor: float = 1.0  # YaRN factor (1 = plain RoPE)
+    rope_orig_len: int = 0  # YaRN original context length
     swa: str = "act"  # window-row storage: "act" (the activation dtype) or "fp8" (E4M3 bytes)
     description: str = ""
 
@@ -131,6 +133,14 @@ WORKLOADS["fp4_1m_pages"] = replace(
     "FP4 indexer K per 32, FP8 (E4M3) window rows, HSI",
 )
 
+# The 1M decode in the pages' storage format with their RoPE extension: YaRN
+# from an original length of 65536 by a factor of 16, i.e. to 1048576
+# positions (zartbot walkthrough, section 1.2).
+WORKLOADS["fp4_1m_yarn"] = replace(
+    WORKLOADS["fp4_1m_pages"], name="fp4_1m_yarn", rope_factor=16.0, rope_orig_len=65536,
+    description="long-context decode, pages' storage format, YaRN RoPE (65536 x 16): 2 x 1048576, HSI",
+)
+
 # Decoder-side chunked prefill: ratio 1, every query of the chunk builds its
 # own HSI pool in the Full layer and the Reindex layers rescore each query's
 # pool with their own indexer queries (zartbot walkthrough, sections 2.3.3
@@ -165,6 +175,12 @@ SMALL = {
     "multi_q_small": replace(WORKLOADS["decode_32k"], name="multi_q_small", batch=2, prior=2990, new=10, n_q=10),
     "encoder_block_small": replace(WORKLOADS["prefill_128k"], name="encoder_block_small", prior=4096, new=512,
                                    n_q=512, layers=ENCODER_BLOCK),
+    # YaRN rotary extension (original length 65536, factor 16; theta 160000)
+    "tiny_yarn": replace(WORKLOADS["tiny_encoder"], name="tiny_yarn", rope_factor=4.0, rope_orig_len=256),
+    "decode_yarn": replace(WORKLOADS["decode_32k"], name="decode_yarn", batch=2, prior=5000, new=1,
+                           rope_theta=160000.0, rope_factor=16.0, rope_orig_len=65536),
+    "prefill_yarn": replace(WORKLOADS["prefill_128k"], name="prefill_yarn", prior=4096, new=512, n_q=512,
+                            rope_theta=160000.0, rope_factor=16.0, rope_orig_len=65536),
     "decoder_prefill_small": replace(WORKLOADS["decoder_prefill_64k"], name="decoder_prefill_small", prior=8192,
                                      new=256, n_q=256, cand_blocks=64, topk=128),
     # FP8 (E4M3) window rows on every attention path: float32 generic, bf16

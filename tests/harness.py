@@ -151,7 +151,7 @@ def check_step(step, inp, seqs=None, caches=None, queries=None):
                 else:
                     assert np.array_equal(top, gpu_topk[plan.source][b, qi]), f"{tag}: Reuse indices differ from source"
                 rows = oc.gather_rows(cache, top, spec.swa[i], int(spec.swa_first[i]), t, wl.window)
-                o, p, ls = oc.attention(spec.q[i, qi], t, rows, wl.d_rope, wl.rope_theta)
+                o, p, ls = oc.attention(spec.q[i, qi], t, rows, wl.d_rope, driver.rope_cfg(wl))
                 err, rl2 = check_outputs(out[b, qi], o, wl, tag)
                 summary["max_abs"] = max(summary["max_abs"], err)
                 summary["rel_l2"] = max(summary["rel_l2"], rl2)

@@ -67,7 +67,8 @@ def call_index(d=None, c=None, ws=FAKE, ws_bytes=1 << 40, pool_in=None, pool_out
         (dict(act_dtype=7), {}, -2),
         (dict(rope_theta=0.0), {}, -1),
         (dict(swa_dtype=B.FP4), {}, -2),
-        (dict(reserved0=1), {}, -1),
+        (dict(rope_factor=0.5), {}, -1),
+        (dict(rope_factor=16.0, rope_orig_len=0), {}, -1),
         ({}, dict(ratio=3), -2),
         ({}, dict(kv_dtype=9), -2),
         ({}, dict(capacity=(1 << 20) + 1), -2),

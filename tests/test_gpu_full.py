@@ -26,6 +26,7 @@ FULL = {
     "encoder_block_128k": ([0], [0, 2047, 4095]),
     "fp4_1m_pages": ([0], None),
     "decoder_prefill_64k": ([0], [0, 2049, 4095]),
+    "fp4_1m_yarn": ([1], None),
 }
 
 

@@ -284,3 +284,46 @@ def test_cache_is_post_rope_and_index_k_from_unrounded_entry():
     assert np.allclose(np.linalg.norm(e_hat, axis=1), np.linalg.norm(e, axis=1))
     assert np.array_equal(main, formats.f32_round(e_hat))
     assert np.array_equal(idx, formats.f32_round(e_hat @ inp.w_ik().astype(np.float64)))
+
+
+# ---- YaRN rotary extension ([ZB] 1.2 names original length 65536, factor 16)
+
+YARN = csa2.Rope(160000.0, 16.0, 65536)
+
+
+def test_yarn_off_is_plain_rope():
+    x = np.random.default_rng(11).standard_normal((3, 64))
+    for off in (csa2.Rope(10000.0, 1.0, 65536), csa2.Rope(10000.0, 0.0, 0)):
+        assert np.array_equal(csa2.rope_freqs(off, 16), csa2.rope_freqs(10000.0, 16))
+        assert np.array_equal(csa2.rope(x, 77, 16, off), csa2.rope(x, 77, 16, 10000.0))
+        assert csa2.logit_temperature(off) == 1.0
+
+
+def test_yarn_keeps_short_wavelengths_and_stretches_long_ones():
+    plain = csa2.rope_freqs(YARN.theta, 64)
+    f = csa2.rope_freqs(YARN, 64)
+    fits = YARN.orig_len * plain / (2 * np.pi)  # wavelengths inside the original context
+    assert np.array_equal(f[fits >= 32], plain[fits >= 32])  # short wavelengths untouched
+    assert np.allclose(f[fits <= 1], plain[fits <= 1] / YARN.factor, rtol=1e-15, atol=0)  # long: interpolated
+    mid = (fits > 1) & (fits < 32)
+    assert mid.any() and (fits >= 32).any() and (fits <= 1).any()  # all three regimes occur at d_rope 64
+    assert np.all(f[mid] < plain[mid]) and np.all(f[mid] > plain[mid] / YARN.factor)
+    assert np.all(np.diff(f) < 0)  # still strictly decreasing over the pairs
+    # the wavelength of the longest interpolated pair grows by the factor: it spans
+    # factor x the original context that the plain one spanned
+    assert np.isclose(2 * np.pi / f[-1], YARN.factor * 2 * np.pi / plain[-1], rtol=1e-14)
+
+
+def test_yarn_rotation_is_relative_and_norm_preserving():
+    rng = np.random.default_rng(12)
+    q, k = rng.standard_normal((2, 128))
+    a = csa2.rope(q, 900_000, 64, YARN) @ csa2.rope(k, 899_500, 64, YARN)
+    b = csa2.rope(q, 1500, 64, YARN) @ csa2.rope(k, 1000, 64, YARN)
+    assert np.isclose(a, b, rtol=1e-9, atol=1e-9)
+    x = rng.standard_normal((4, 128))
+    assert np.allclose(np.linalg.norm(csa2.rope(x, 1_000_000, 64, YARN), axis=1), np.linalg.norm(x, axis=1))
+
+
+def test_yarn_temperature_grows_with_the_factor():
+    ts = [csa2.logit_temperature(csa2.Rope(10000.0, s, 65536)) for s in (1.0, 2.0, 4.0, 16.0, 64.0)]
+    assert ts[0] == 1.0 and all(b > a for a, b in zip(ts, ts[1:]))
