@@ -12,8 +12,10 @@ Modules:
 
 Parity pins: every function is pinned by a CPU test against something other
 than itself (enumerated tables, library conversions, brute force, closed
-forms, invariants), except the indexer-score formula, whose form the pages do
-not print: "parity unpinned" for the formula itself (its invariants are
-still tested).
+forms, invariants), except two formulas the pages do not print, which are
+"parity unpinned" for their form (their invariants are still tested): the
+indexer score, and the YaRN rotary interpolation and temperature
+(``csa2.rope_freqs``, ``csa2.logit_temperature``), of which the pages give
+only the original length and the factor.
 """
 from . import csa2, footprint, formats  # noqa: F401
