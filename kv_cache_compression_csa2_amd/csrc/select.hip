@@ -44,6 +44,7 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 constexpr int kNT = 1024;
 constexpr int kNW = kNT / kWave;
 constexpr int kMaxCand = 16384;
+constexpr int kSmallCand = 4096;  // LDS key capacity of the 64-register variant
 constexpr int kMaxList = 2048;
 constexpr int kBins = 2048;
 constexpr int kBinsPerWave = kBins / kNW;  // 128: two per lane
@@ -82,7 +83,12 @@ __device__ __forceinline__ uint32_t waves_before(const SelLds L, int base, int w
 // are zero on entry and on exit.
 //
 // Thread t owns the run of R consecutive positions [R t, R t + R) (R a
-// multiple of 4, at most 16), read 16 bytes at a time.  The threshold key T
+// multiple of 4, at most KR = the LDS key capacity / 1024), read 16 bytes at
+// a time into registers once: every pass and both compaction steps then work
+// on registers (re-reading them from LDS made each step wait for an LDS round
+// trip per 4 keys, which measured ~1.5 us per pass on 16384 keys).  Positions
+// at or past n hold the invalid key, so the loops run over all KR registers
+// without bounds tests.  The threshold key T
 // is found by narrowing a key interval [lo, hi] that holds it: each pass
 // splits the interval into at most 2048 equal bins (8192 for 2049..4096 keys
 // of which at most a quarter are selected), and the interval shrinks
@@ -92,11 +98,21 @@ __device__ __forceinline__ uint32_t waves_before(const SelLds L, int base, int w
 // histogram (by wave) cut the LDS atomic collisions of clustered keys; three
 // passes always suffice for 32-bit keys.  The compaction is one block-wide
 // scan of packed (greater, equal) counts, then a short walk per thread.
-template <bool FINE>
+template <bool FINE, int KR>
 __device__ int select_top_impl(const SelLds L, int n, int m, lds_u32* out) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int R = ((((n + kNT - 1) / kNT) + 3) & ~3);
   const int p0 = R * tid;
+  uint32_t kr[KR];
+#pragma unroll
+  for (int v = 0; v < KR; v += 4) {
+    // p0 + v < n <= capacity and both are multiples of 4: the 16 bytes lie inside keys[]
+    const u32x4 k4 = (v < R && p0 + v < n) ? *reinterpret_cast<const lds_u32x4*>(L.keys + p0 + v)
+                                           : u32x4{kKeyNegInf, kKeyNegInf, kKeyNegInf, kKeyNegInf};
+    const uint32_t kk[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kr[v + i] = (v < R && p0 + v + i < n) ? kk[i] : kKeyNegInf;
+  }
   constexpr int bin_bits = FINE ? 13 : 11;
   lds_u32* const hist = FINE ? L.hist : L.hist + kBins * (w & 3);
 
@@ -111,15 +127,10 @@ __device__ int select_top_impl(const SelLds L, int n, int m, lds_u32* out) {
       const uint64_t width = uint64_t(hi) - lo + 1;
       const int bits = 64 - __clzll(width - 1);  // bits spanned by the interval
       const int shift = bits > bin_bits ? bits - bin_bits : 0;
-      for (int v = 0; v < R; v += 4) {
-        if (p0 + v >= n) break;
-        const u32x4 k4 = *reinterpret_cast<const lds_u32x4*>(L.keys + p0 + v);
-        const uint32_t kk[4] = {k4.x, k4.y, k4.z, k4.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t k = kk[i];
-          if (p0 + v + i < n && k > kKeyNegInf && k >= lo && k <= hi) lds_inc(&hist[(k - lo) >> shift]);
-        }
+      for (int i = 0; i < KR; ++i) {
+        const uint32_t k = kr[i];
+        if (k > kKeyNegInf && k >= lo && k <= hi) lds_inc(&hist[(k - lo) >> shift]);
       }
       __syncthreads();
       // lane `lane` of wave w holds nb consecutive bins from b0 (fine: 8 of
@@ -188,16 +199,10 @@ __device__ int select_top_impl(const SelLds L, int n, int m, lds_u32* out) {
 
   // order-preserving compaction: (greater, equal) counts packed 16:16, one block scan
   uint32_t gt = 0, eq = 0;  // T >= kKeyNegInf, so k > T implies a valid key
-  for (int v = 0; v < R; v += 4) {
-    if (p0 + v >= n) break;
-    const u32x4 k4 = *reinterpret_cast<const lds_u32x4*>(L.keys + p0 + v);
-    const uint32_t kk[4] = {k4.x, k4.y, k4.z, k4.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t k = p0 + v + i < n ? kk[i] : kKeyNegInf;
-      gt += k > T;
-      eq += k == T && k > kKeyNegInf;
-    }
+  for (int i = 0; i < KR; ++i) {
+    gt += kr[i] > T;
+    eq += kr[i] == T && kr[i] > kKeyNegInf;
   }
   const uint32_t packed = (gt << 16) | eq;
   const uint32_t incl = __ockl_wfscan_add_u32(packed, true);
@@ -210,20 +215,15 @@ __device__ int select_top_impl(const SelLds L, int n, int m, lds_u32* out) {
   const uint32_t before = before_w + incl - packed;
   uint32_t gt_run = before >> 16, eq_run = before & 0xFFFFu;
   const uint32_t chosen = (all >> 16) + min(all & 0xFFFFu, need);
-  for (int v = 0; v < R; v += 4) {
-    if (p0 + v >= n) break;
-    const u32x4 k4 = *reinterpret_cast<const lds_u32x4*>(L.keys + p0 + v);
-    const uint32_t kk[4] = {k4.x, k4.y, k4.z, k4.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t k = p0 + v + i < n ? kk[i] : kKeyNegInf;
-      const bool g = k > T, e = k == T && k > kKeyNegInf;
-      // a greater key goes after the equal keys taken so far, an equal key
-      // is taken while fewer than `need` equal keys precede it
-      if (g || (e && eq_run < need)) out[gt_run + min(eq_run, need)] = uint32_t(p0 + v + i);
-      gt_run += g;
-      eq_run += e;
-    }
+  for (int i = 0; i < KR; ++i) {
+    const uint32_t k = kr[i];
+    const bool g = k > T, e = k == T && k > kKeyNegInf;
+    // a greater key goes after the equal keys taken so far, an equal key
+    // is taken while fewer than `need` equal keys precede it
+    if (g || (e && eq_run < need)) out[gt_run + min(eq_run, need)] = uint32_t(p0 + i);
+    gt_run += g;
+    eq_run += e;
   }
   __syncthreads();
   return int(chosen);
@@ -236,15 +236,15 @@ __device__ int select_top_impl(const SelLds L, int n, int m, lds_u32* out) {
 // measured slower there (a threshold in the dense middle, or 2048 clustered
 // pool maxima, still needs a second pass).
 __device__ __attribute__((noinline)) int select_top(const SelLds L, int n, int m, lds_u32* out) {
-  if (n > 2048 && n <= 4096 && 4 * m <= n) return select_top_impl<true>(L, n, m, out);
-  return select_top_impl<false>(L, n, m, out);
+  if (n > 2048 && n <= 4096 && 4 * m <= n) return select_top_impl<true, kMaxCand / kNT>(L, n, m, out);
+  return select_top_impl<false, kMaxCand / kNT>(L, n, m, out);
 }
 // The same, inlined: the 64-register variant of the kernel must not call a
 // function that allocates beyond that (the full variant keeps the call, whose
 // code measured ~2 us faster per pool selection)
 __device__ __forceinline__ int select_top_inl(const SelLds L, int n, int m, lds_u32* out) {
-  if (n > 2048 && n <= 4096 && 4 * m <= n) return select_top_impl<true>(L, n, m, out);
-  return select_top_impl<false>(L, n, m, out);
+  if (n > 2048 && n <= 4096 && 4 * m <= n) return select_top_impl<true, kSmallCand / kNT>(L, n, m, out);
+  return select_top_impl<false, kSmallCand / kNT>(L, n, m, out);
 }
 
 // Key of a[i]; an index outside [0, n) (never produced by a correct
@@ -455,7 +455,6 @@ __device__ __forceinline__ void select_body(int topk, int cand_blocks, int ratio
 #define SELECT_PASS \
   topk, cand_blocks, ratio, capacity, q_pos, n_q, pool_in, n_entries, scores, bmax, sbmax, dom_cap, topk_out, pool_out, topk_scores
 
-constexpr int kSmallCand = 4096;
 __global__ __launch_bounds__(kNT) void select_kernel(SELECT_ARGS) { select_body<kMaxCand>(SELECT_PASS); }
 // two workgroups per compute unit: 32 waves, at most 64 registers each
 __global__ __launch_bounds__(kNT) __attribute__((amdgpu_num_vgpr(64))) void select_kernel_wide(SELECT_ARGS) {
