@@ -199,6 +199,64 @@ def run_gpu(wl, steps: int, warmup: int, copies: int, use_graph: bool):
     return ms, launches
 
 
+def run_oproj(n_tok: int, steps: int, warmup: int, copies: int) -> dict:
+    """The grouped output projection alone at the production shape (64 heads
+    x 512 into 8 groups of rank 1024) for n_tok attention-output rows;
+    `copies` weight sets are rotated so the Infinity Cache cannot hold them."""
+    import torch
+
+    import synth
+    from kv_cache_compression_csa2_amd import binding as B
+
+    width, groups, rank = 64 * 512, 8, 1024
+    x, w = synth.oproj_inputs(n_tok, width, groups, rank, "bf16")
+    xd = torch.from_numpy(x).to("cuda").to(torch.bfloat16)
+    ws = [torch.from_numpy(w).to("cuda").to(torch.bfloat16) for _ in range(copies)]
+    y = torch.empty((n_tok, groups * rank), dtype=torch.bfloat16, device="cuda")
+    del x, w
+
+    def one(i):
+        B.csa2_grouped_out_proj(B.BF16, n_tok, width, groups, rank, xd, ws[i % copies], y)
+
+    for i in range(warmup):
+        one(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        one(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    B.csa2_trace_enable(steps)
+    for i in range(steps):
+        one(i)
+    torch.cuda.synchronize()
+    recs, dropped = B.csa2_trace_read(steps)
+    B.csa2_trace_enable(0)
+    if dropped or len(recs) != steps:
+        raise RuntimeError(f"kernel trace incomplete: {len(recs)} records, {dropped} dropped")
+    kname = recs[0][0]
+    kms = sum(r[1] for r in recs) / steps
+    wbytes = groups * rank * (width // groups) * 2
+    nbytes = wbytes + n_tok * width * 2 + n_tok * groups * rank * 2
+    flops = 2 * n_tok * width * rank
+    if n_tok <= 64:
+        achieved = nbytes / (kms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "per_launch": nbytes, "avg_ms": round(kms, 5),
+                "traffic": None}
+    else:
+        achieved = flops / (kms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": kname, "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "per_launch": flops,
+                "avg_ms": round(kms, 5), "traffic": None}
+    return {"metric": "grouped_out_proj_tokens_per_s", "value": round(n_tok / (kms * 1e-3), 1), "unit": "tokens/s",
+            "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_launch_wall": round(ms, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"grouped_out_proj_{n_tok}", "tokens": n_tok, "width": width, "groups": groups,
+                       "rank": rank, "weight_copies": copies},
+            "roofline": roof, "cpu_baseline": None}
+
+
 def cpu_baseline(wl, seconds: float) -> dict:
     """The float64 oracle timed on the host cores on a sample of the workload's sequences."""
     import numpy as np
@@ -245,12 +303,19 @@ def main() -> int:
     ap.add_argument("--eager", action="store_true", help="launch the timed steps directly instead of replaying HIP graphs")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--oproj-tokens", type=int, default=0,
+                    help="time only the grouped output projection, for this many attention-output rows")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB 5 times (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
         return 2
+
+    if args.oproj_tokens:
+        out = run_oproj(args.oproj_tokens, args.steps, args.warmup, max(args.copies, 6))
+        print(json.dumps(out), flush=True)
+        return 0
 
     import synth
 

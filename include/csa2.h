@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 2
+#define CSA2_ABI_VERSION 3
 
 typedef enum csa2_status {
   CSA2_OK = 0,
@@ -263,6 +263,30 @@ int csa2_layer_group(const csa2_dims* dims, const csa2_kv_cache* cache, int32_t 
                      const csa2_layer* layers, const int32_t* q_pos, int32_t n_q,
                      const csa2_compress_args* compress, void* ws, size_t ws_bytes, void* stream);
 
+/* csa2_grouped_out_proj - the grouped low-rank output projection after the
+ * attention ([ZB] 1.2: o_lora_rank 1024 in o_groups 8).
+ *
+ * The width = n_heads * d channels of an attention output row split into
+ * n_groups contiguous slices of K = width / n_groups (the outputs of
+ * n_heads / n_groups heads); group g maps its slice to `rank` outputs with its
+ * own matrix:
+ *   y[t][g*rank + r] = sum_c x[t][g*K + c] * w[g][r][c]
+ * accumulated in float32 and stored in act_dtype (bf16: round to nearest
+ * even).  The rank outputs of the groups are concatenated.
+ *
+ *  act_dtype  CSA2_F32 or CSA2_BF16, for x, w and y
+ *  n_tok      rows of x and y (batch * n_q for a csa2_sparse_attn output); 0 does nothing
+ *  x          [n_tok][width] act: the attention output, read only
+ *  w          [n_groups][rank][K] act: each output's weights over its group's slice, read only
+ *  y          [n_tok][n_groups*rank] act, written; must not overlap x or w
+ * width must be a positive multiple of n_groups, rank positive; x, w and y
+ * device pointers, 16-byte aligned.  bf16 with K a multiple of 64 and rank a
+ * multiple of 32 runs on the matrix cores; other shapes run a plain kernel.
+ * No workspace; nothing is allocated.  Returns a csa2_status.
+ */
+int csa2_grouped_out_proj(int32_t act_dtype, int32_t n_tok, int32_t width, int32_t n_groups, int32_t rank,
+                          const void* x, const void* w, void* y, void* stream);
+
 /* Bytes of workspace an entry point needs for n_q queries per sequence, or 0
  * if the arguments are invalid (csa2_last_error() then says why).  Sized
  * from cache->capacity and cache->batch. */
@@ -296,7 +320,9 @@ typedef enum csa2_kernel {
   CSA2_KERNEL_ATTN_FP4 = 8,       /* attn_mfma_kernel over an FP4 cache, scales per 32 */
   CSA2_KERNEL_ATTN_MERGE = 9,     /* attn_merge_kernel */
   CSA2_KERNEL_ATTN_FP4_G16 = 10,  /* attn_mfma_kernel over an FP4 cache, scales per 16 */
-  CSA2_KERNEL_SCAN_PREFILL = 11   /* scan_prefill_kernel (many queries per sequence) */
+  CSA2_KERNEL_SCAN_PREFILL = 11,  /* scan_prefill_kernel (many queries per sequence) */
+  CSA2_KERNEL_OPROJ_MFMA = 12,    /* oproj_mfma_kernel (bf16 grouped output projection) */
+  CSA2_KERNEL_OPROJ_GENERIC = 13  /* oproj_generic_kernel */
 } csa2_kernel;
 
 typedef struct csa2_trace_record {

@@ -365,4 +365,30 @@ int csa2_layer_group(const csa2_dims* dims, const csa2_kv_cache* cache, int32_t 
   }
 }
 
+int csa2_grouped_out_proj(int32_t act_dtype, int32_t n_tok, int32_t width, int32_t n_groups, int32_t rank,
+                          const void* x, const void* w, void* y, void* stream) {
+  g_last_error.clear();
+  try {
+    if (act_dtype != CSA2_F32 && act_dtype != CSA2_BF16)
+      return fail(CSA2_ERR_UNSUPPORTED, "act_dtype=%d: the projection takes F32 or BF16", act_dtype);
+    if (n_tok < 0 || width <= 0 || n_groups <= 0 || rank <= 0)
+      return fail(CSA2_ERR_INVALID_ARG, "n_tok=%d width=%d n_groups=%d rank=%d: n_tok must be >= 0, the rest > 0",
+                  n_tok, width, n_groups, rank);
+    if (width % n_groups)
+      return fail(CSA2_ERR_INVALID_ARG, "width=%d is not a multiple of n_groups=%d", width, n_groups);
+    if (int64_t(n_groups) * rank > (int64_t(1) << 30) || int64_t(rank) * width > (int64_t(1) << 40))
+      return fail(CSA2_ERR_UNSUPPORTED, "n_groups*rank=%lld too large", (long long)(int64_t(n_groups) * rank));
+    if (n_tok == 0) return CSA2_OK;
+    if (!x || !w || !y) return fail(CSA2_ERR_INVALID_ARG, "x, w and y are required");
+    if (!aligned16(x) || !aligned16(w) || !aligned16(y))
+      return fail(CSA2_ERR_INVALID_ARG, "x, w and y must be 16-byte aligned");
+    clear_stale_error();
+    const hipError_t e = csa2::launch_oproj(act_dtype, n_tok, width, n_groups, rank, x, w, y,
+                                            static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? CSA2_OK : fail_hip(e, "output projection launch");
+  } catch (...) {
+    return fail(CSA2_ERR_HIP, "internal exception");
+  }
+}
+
 }  // extern "C"

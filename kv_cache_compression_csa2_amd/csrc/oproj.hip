@@ -1,0 +1,171 @@
+// Grouped low-rank output projection after the attention.
+//
+// Pages: zartbot walkthrough (hn.213312.xyz) section 1.2: the output
+// projection is split into o_groups = 8 groups, with o_lora_rank = 1024 per
+// group.  Group g takes its own contiguous slice of the concatenated head
+// outputs (n_heads / o_groups heads, K = n_heads d / o_groups channels) to
+// `rank` outputs:
+//   y[t][g rank + r] = sum_c x[t][g K + c] * w[g][r][c]
+// with float32 accumulation, stored in the activation type (bf16: round to
+// nearest even).
+//
+// The bf16 kernel is a matrix-core contraction.  A workgroup computes a tile
+// of 32 tokens x NT*32 outputs of one group; its 8 waves split the group's K
+// channels into 64-channel chunks (wave w takes chunks w, w + 8, ...) and
+// their partial tiles are summed through LDS.  In decode (a few tokens) the
+// kernel streams the 8 x 1024 x 4096 weights once, so it is HBM-bound: the
+// K split keeps 8 waves of loads in flight per compute unit, and each lane
+// reads 64 contiguous bytes of a token row and of a weight row per chunk.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace csa2 {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
+typedef float f32x16_t __attribute__((__vector_size__(64)));
+
+constexpr int kOpWaves = 8;
+constexpr int kOpThreads = kOpWaves * kWave;
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// One 64-channel chunk of a lane's operands: A from the token row, B from
+// NT weight rows.  Lane (i, h) (i = lane % 32, h = lane / 32) holds channels
+// 32 h + 8 u .. 32 h + 8 u + 7 of the chunk in element u of each array, and
+// product u of the chunk contracts exactly those channels on both sides.
+template <int NT>
+struct OpChunk {
+  uint4 a[4];
+  uint4 b[NT][4];
+};
+
+// NT: 32-output tiles per wave (1 in decode, where the grid must still cover
+// the chip; 2 with many tokens, halving the token-row reads per output).
+template <int NT>
+__global__ __launch_bounds__(kOpThreads) void oproj_mfma_kernel(int n_tok, int width, int rank,
+                                                                const uint16_t* __restrict__ x,
+                                                                const uint16_t* __restrict__ w, uint16_t* __restrict__ y) {
+  extern __shared__ float red[];  // [kOpWaves][NT][16][64]
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int i = lane & 31, h = lane >> 5;
+  const int t0 = blockIdx.x * 32, r0 = blockIdx.y * 32 * NT, g = blockIdx.z;
+  const int n_groups = gridDim.z;
+  const int K = width / n_groups, nchunk = K / 64;
+
+  // rows past the last token repeat it; their products are never stored
+  const uint16_t* xrow = x + int64_t(min(t0 + i, n_tok - 1)) * width + int64_t(g) * K + 32 * h;
+  const uint16_t* wrow[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) wrow[t] = w + (int64_t(g) * rank + r0 + 32 * t + i) * K + 32 * h;
+
+  auto issue = [&](int c, OpChunk<NT>& ch) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) ch.a[u] = *reinterpret_cast<const uint4*>(xrow + 64 * c + 8 * u);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) ch.b[t][u] = *reinterpret_cast<const uint4*>(wrow[t] + 64 * c + 8 * u);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  f32x16_t acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
+
+  // keep: all ones, or zero for a chunk past the wave's range (its products
+  // then add zero; a branch instead would let the compiler sink the chunk's
+  // loads into it, after the other buffer's wait)
+  auto contract = [&](const OpChunk<NT>& ch, uint32_t keep) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint4 a = {ch.a[u].x & keep, ch.a[u].y & keep, ch.a[u].z & keep, ch.a[u].w & keep};
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(ch.b[t][u]), acc[t], 0, 0, 0);
+    }
+  };
+
+  // one chunk in flight while the other is contracted, in two fixed buffers
+  // (a copy from the prefetch buffer would make the compiler wait for the
+  // prefetch); the loads are unconditional (a wave past its last chunk
+  // re-reads a valid one and never uses it), so the wait counts stay exact
+  OpChunk<NT> b0, b1;
+  issue(min(wv, nchunk - 1), b0);
+  for (int c = wv; c < nchunk; c += 2 * kOpWaves) {
+    issue(min(c + kOpWaves, nchunk - 1), b1);
+    contract(b0, ~0u);
+    issue(min(c + 2 * kOpWaves, nchunk - 1), b0);
+    contract(b1, c + kOpWaves < nchunk ? ~0u : 0u);
+  }
+
+  // partial tiles of the waves, summed through LDS (lane-contiguous: no bank conflicts)
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[((wv * NT + t) * 16 + r) * 64 + lane] = acc[t][r];
+  __syncthreads();
+  const int out_w = n_groups * rank;
+  for (int o = threadIdx.x; o < NT * 1024; o += kOpThreads) {
+    const int t = o >> 10, r = (o >> 6) & 15, l = o & 63;
+    float s = 0.0f;
+#pragma unroll
+    for (int v = 0; v < kOpWaves; ++v) s += red[((v * NT + t) * 16 + r) * 64 + l];
+    // product element r of lane l: row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
+    const int row = 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+    const int tok = t0 + row;
+    if (tok < n_tok) y[int64_t(tok) * out_w + int64_t(g) * rank + r0 + 32 * t + (l & 31)] = f32_to_bf16(s);
+  }
+}
+
+// Any shape and either activation type: one thread per output, float32
+// accumulation in channel order.
+__global__ __launch_bounds__(256) void oproj_generic_kernel(int n_tok, int width, int n_groups, int rank, int act_bf16,
+                                                            const void* __restrict__ x, const void* __restrict__ w,
+                                                            void* __restrict__ y) {
+  const int64_t out_w = int64_t(n_groups) * rank;
+  const int64_t o = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (o >= int64_t(n_tok) * out_w) return;
+  const int64_t tok = o / out_w, col = o % out_w;
+  const int64_t g = col / rank, r = col % rank;
+  const int64_t K = width / n_groups;
+  const int64_t xo = tok * width + g * K, wo = (g * rank + r) * K;
+  float s = 0.0f;
+  for (int64_t c = 0; c < K; ++c) s = fmaf(act_load(x, xo + c, act_bf16), act_load(w, wo + c, act_bf16), s);
+  if (act_bf16)
+    static_cast<uint16_t*>(y)[o] = f32_to_bf16(s);
+  else
+    static_cast<float*>(y)[o] = s;
+}
+
+constexpr size_t oproj_lds(int nt) { return sizeof(float) * kOpWaves * nt * 16 * 64; }
+
+}  // namespace
+
+hipError_t launch_oproj(int32_t act_dtype, int32_t n_tok, int32_t width, int32_t n_groups, int32_t rank,
+                        const void* x, const void* w, void* y, hipStream_t stream) {
+  if (n_tok == 0) return hipSuccess;
+  const int64_t K = width / n_groups;
+  if (act_dtype == CSA2_BF16 && K % 64 == 0 && rank % 32 == 0) {
+    // two output tiles per wave once one-tile workgroups would fill the chip several times over
+    const int64_t tok_tiles = (n_tok + 31) / 32;
+    const bool two = rank % 64 == 0 && tok_tiles * (rank / 32) * n_groups >= 4 * 256;
+    const dim3 grid(uint32_t(tok_tiles), uint32_t(rank / (two ? 64 : 32)), uint32_t(n_groups));
+    const auto* xb = static_cast<const uint16_t*>(x);
+    const auto* wb = static_cast<const uint16_t*>(w);
+    auto* yb = static_cast<uint16_t*>(y);
+    if (two)
+      return launch_kernel(CSA2_KERNEL_OPROJ_MFMA, oproj_mfma_kernel<2>, grid, dim3(kOpThreads), oproj_lds(2), stream,
+                           int(n_tok), int(width), int(rank), xb, wb, yb);
+    return launch_kernel(CSA2_KERNEL_OPROJ_MFMA, oproj_mfma_kernel<1>, grid, dim3(kOpThreads), oproj_lds(1), stream,
+                         int(n_tok), int(width), int(rank), xb, wb, yb);
+  }
+  const int64_t total = int64_t(n_tok) * n_groups * rank;
+  return launch_kernel(CSA2_KERNEL_OPROJ_GENERIC, oproj_generic_kernel, dim3(uint32_t((total + 255) / 256)), dim3(256),
+                       0, stream, int(n_tok), int(width), int(n_groups), int(rank), act_dtype == CSA2_BF16 ? 1 : 0, x,
+                       w, y);
+}
+
+}  // namespace csa2

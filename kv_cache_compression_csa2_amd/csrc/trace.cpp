@@ -130,6 +130,8 @@ const char* csa2_kernel_name(int32_t kernel) {
     case CSA2_KERNEL_ATTN_MERGE: return "attn_merge_kernel";
     case CSA2_KERNEL_ATTN_FP4_G16: return "attn_mfma_kernel<true, 16>";
     case CSA2_KERNEL_SCAN_PREFILL: return "scan_prefill_kernel";
+    case CSA2_KERNEL_OPROJ_MFMA: return "oproj_mfma_kernel";
+    case CSA2_KERNEL_OPROJ_GENERIC: return "oproj_generic_kernel";
     default: return "unknown";
   }
 }

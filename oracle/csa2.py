@@ -375,6 +375,26 @@ def attention(q: np.ndarray, t: int, rows: np.ndarray, d_rope: int, theta):
     return out, p, lse
 
 
+def grouped_out_proj(x: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """The grouped low-rank output projection after the attention (zartbot
+    walkthrough, section 1.2: o_lora_rank 1024 in o_groups 8).
+
+    ``x`` [n, G*K]: attention output rows, the heads' outputs concatenated;
+    ``w`` [G, R, K]: group g's R outputs, each a weight row over the group's
+    own K channels.  Group g maps channels [g K, g K + K) of a row to outputs
+    [g R, g R + R): y[:, gR:gR+R] = x[:, gK:gK+K] w[g]^T.  float64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    G, R, K = w.shape
+    if x.shape[1] != G * K:
+        raise ValueError(f"x has {x.shape[1]} channels, groups need {G} x {K}")
+    y = np.empty((x.shape[0], G * R))
+    for g in range(G):
+        y[:, g * R:(g + 1) * R] = x[:, g * K:(g + 1) * K] @ w[g].T
+    return y
+
+
 def gather_rows(cache: "SeqCache", topk: np.ndarray, swa: np.ndarray, swa_first: int, t: int, window: int):
     """Rows one query reads: selected main-KV rows (skipping -1), then its window rows.
 

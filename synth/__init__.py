@@ -290,5 +290,18 @@ class Inputs:
         return rows, firsts
 
 
+def oproj_inputs(n_tok: int, width: int, n_groups: int, rank: int, act: str, seed: int = 0):
+    """Seeded inputs of the grouped output projection: attention-output rows
+    x [n_tok, width] (each channel a convex mix of unit-variance latent
+    values: N(0, 0.25)) and group weights w [n_groups, rank, width/n_groups]
+    with std 1/sqrt(K), both exact in the activation type."""
+    k = width // n_groups
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(_key(seed, "oproj", n_tok, width, n_groups, rank))))
+    x = rng.standard_normal((n_tok, width), dtype=np.float32) * np.float32(0.5)
+    w = rng.standard_normal((n_groups, rank, k), dtype=np.float32) * np.float32(1.0 / np.sqrt(k))
+    x, w = round_act(x, act), round_act(w, act)
+    return x, w
+
+
 def get(name: str) -> Workload:
     return ALL[name]

@@ -28,7 +28,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert B.csa2_abi_version() == 2
+    assert B.csa2_abi_version() == 3
     assert B.status_str(0) == "CSA2_OK"
     assert B.status_str(-4) == "CSA2_ERR_MODE_ORDER"
     assert B.status_str(-99) == "CSA2_ERR_UNKNOWN"
@@ -181,3 +181,25 @@ def test_trace_api_without_launches():
     st = lib.csa2_trace_enable(4)  # no device here: a HIP error; with one: enabled
     assert st in (0, -5)
     assert lib.csa2_trace_enable(0) == 0
+
+
+@pytest.mark.parametrize("args, status", [
+    ((B.FP4, 4, 512, 8, 64), -2),   # cache-only dtype
+    ((B.BF16, 4, 500, 8, 64), -1),  # width not a multiple of the groups
+    ((B.BF16, -1, 512, 8, 64), -1),
+    ((B.BF16, 4, 512, 0, 64), -1),
+    ((B.BF16, 4, 512, 8, 0), -1),
+])
+def test_grouped_out_proj_rejects_bad_arguments(args, status):
+    lib = B.library()
+    assert lib.csa2_grouped_out_proj(*args, FAKE, FAKE, FAKE, None) == status
+    assert B.last_error()
+
+
+def test_grouped_out_proj_checks_pointers_and_allows_no_tokens():
+    lib = B.library()
+    assert lib.csa2_grouped_out_proj(B.BF16, 4, 512, 8, 64, None, FAKE, FAKE, None) == -1
+    assert lib.csa2_grouped_out_proj(B.BF16, 4, 512, 8, 64, FAKE + 2, FAKE, FAKE, None) == -1
+    # no tokens: nothing to do, no pointer needed, no GPU call
+    assert lib.csa2_grouped_out_proj(B.BF16, 0, 512, 8, 64, None, None, None, None) == 0
+    assert B.last_error() == ""
