@@ -9,13 +9,17 @@
 // with float32 accumulation, stored in the activation type (bf16: round to
 // nearest even).
 //
-// The bf16 kernel is a matrix-core contraction.  A workgroup computes a tile
-// of 32 tokens x NT*32 outputs of one group; its 8 waves split the group's K
-// channels into 64-channel chunks (wave w takes chunks w, w + 8, ...) and
-// their partial tiles are summed through LDS.  In decode (a few tokens) the
-// kernel streams the 8 x 1024 x 4096 weights once, so it is HBM-bound: the
-// K split keeps 8 waves of loads in flight per compute unit, and each lane
-// reads 64 contiguous bytes of a token row and of a weight row per chunk.
+// The bf16 kernel is a matrix-core contraction in two layouts.  Few tokens
+// (decode): a workgroup computes 32 tokens x 32 outputs of one group, its 16
+// waves split the group's K channels into 64-channel chunks (wave w takes
+// chunks w, w + 16, ...) and their partial tiles are summed through LDS; the
+// kernel streams the 8 x 1024 x 4096 weights once, so it is HBM-bound, and
+// the split keeps 16 waves of loads in flight per compute unit.  Many tokens:
+// a workgroup computes 128 tokens x 128 outputs, its 8 waves as 4 x 2 tiles
+// of 32 x 64 over the whole K, so each token row and weight row a workgroup
+// reads serves 2 or 4 waves (through L1) and no reduction is needed.  Either
+// way each lane reads 64 contiguous bytes of a token row and of each weight
+// row per chunk.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -25,8 +29,6 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
 typedef float f32x16_t __attribute__((__vector_size__(64)));
 
-constexpr int kOpWaves = 8;
-constexpr int kOpThreads = kOpWaves * kWave;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
@@ -40,18 +42,23 @@ struct OpChunk {
   uint4 b[NT][4];
 };
 
-// NT: 32-output tiles per wave (1 in decode, where the grid must still cover
-// the chip; 2 with many tokens, halving the token-row reads per output).
-template <int NT>
-__global__ __launch_bounds__(kOpThreads) void oproj_mfma_kernel(int n_tok, int width, int rank,
-                                                                const uint16_t* __restrict__ x,
-                                                                const uint16_t* __restrict__ w, uint16_t* __restrict__ y) {
-  extern __shared__ float red[];  // [kOpWaves][NT][16][64]
+// NT: 32-output tiles per wave.  SPLITK: WAVES waves share one 32 x NT*32
+// tile and split K; else WAVES = 8 waves tile 128 tokens x 64 NT outputs.
+template <int NT, int WAVES, bool SPLITK>
+__global__ __launch_bounds__(WAVES * kWave) void oproj_mfma_kernel(int n_tok, int width, int rank,
+                                                                   const uint16_t* __restrict__ x,
+                                                                   const uint16_t* __restrict__ w,
+                                                                   uint16_t* __restrict__ y) {
+  static_assert(SPLITK || WAVES == 8, "the tiled layout is 4 x 2 waves");
+  extern __shared__ float red[];  // SPLITK: [WAVES][NT][16][64]
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int i = lane & 31, h = lane >> 5;
-  const int t0 = blockIdx.x * 32, r0 = blockIdx.y * 32 * NT, g = blockIdx.z;
+  const int g = blockIdx.z;
+  const int t0 = SPLITK ? blockIdx.x * 32 : blockIdx.x * 128 + 32 * (wv & 3);
+  const int r0 = SPLITK ? blockIdx.y * 32 * NT : blockIdx.y * 64 * NT + 32 * NT * (wv >> 2);
   const int n_groups = gridDim.z;
   const int K = width / n_groups, nchunk = K / 64;
+  const int c_first = SPLITK ? wv : 0, c_step = SPLITK ? WAVES : 1;
 
   // rows past the last token repeat it; their products are never stored
   const uint16_t* xrow = x + int64_t(min(t0 + i, n_tok - 1)) * width + int64_t(g) * K + 32 * h;
@@ -91,32 +98,115 @@ __global__ __launch_bounds__(kOpThreads) void oproj_mfma_kernel(int n_tok, int w
   // one chunk in flight while the other is contracted, in two fixed buffers
   // (a copy from the prefetch buffer would make the compiler wait for the
   // prefetch); the loads are unconditional (a wave past its last chunk
-  // re-reads a valid one and never uses it), so the wait counts stay exact
+  // re-reads a valid one and never uses it), so the wait counts stay exact.
+  // (A ring of three measured slower at K 4096: 28 against 20 us in decode.)
   OpChunk<NT> b0, b1;
-  issue(min(wv, nchunk - 1), b0);
-  for (int c = wv; c < nchunk; c += 2 * kOpWaves) {
-    issue(min(c + kOpWaves, nchunk - 1), b1);
+  issue(min(c_first, nchunk - 1), b0);
+  for (int c = c_first; c < nchunk; c += 2 * c_step) {
+    issue(min(c + c_step, nchunk - 1), b1);
     contract(b0, ~0u);
-    issue(min(c + 2 * kOpWaves, nchunk - 1), b0);
-    contract(b1, c + kOpWaves < nchunk ? ~0u : 0u);
+    issue(min(c + 2 * c_step, nchunk - 1), b0);
+    contract(b1, c + c_step < nchunk ? ~0u : 0u);
   }
 
-  // partial tiles of the waves, summed through LDS (lane-contiguous: no bank conflicts)
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) red[((wv * NT + t) * 16 + r) * 64 + lane] = acc[t][r];
-  __syncthreads();
+  // product element r of lane l: row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
   const int out_w = n_groups * rank;
-  for (int o = threadIdx.x; o < NT * 1024; o += kOpThreads) {
-    const int t = o >> 10, r = (o >> 6) & 15, l = o & 63;
+  if constexpr (!SPLITK) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int tok = t0 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (tok < n_tok) y[int64_t(tok) * out_w + int64_t(g) * rank + r0 + 32 * t + i] = f32_to_bf16(acc[t][r]);
+      }
+  } else {
+    // partial tiles of the waves, summed through LDS (lane-contiguous: no bank conflicts)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[((wv * NT + t) * 16 + r) * 64 + lane] = acc[t][r];
+    __syncthreads();
+    for (int o = threadIdx.x; o < NT * 1024; o += WAVES * kWave) {
+      const int t = o >> 10, r = (o >> 6) & 15, l = o & 63;
+      float s = 0.0f;
+#pragma unroll
+      for (int v = 0; v < WAVES; ++v) s += red[((v * NT + t) * 16 + r) * 64 + l];
+      const int tok = t0 + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+      if (tok < n_tok) y[int64_t(tok) * out_w + int64_t(g) * rank + r0 + 32 * t + (l & 31)] = f32_to_bf16(s);
+    }
+  }
+}
+
+// At most 16 tokens (decode): the 16 x 16 x 32 product, whose A operand is
+// exactly the 16 token rows.  A workgroup computes the 16 tokens x 32 outputs
+// of one group; its 16 waves split K as above, but each wave issues up to 4
+// chunks at once (6 loads per lane per chunk), so a workgroup asks for its
+// whole weight tile (32 rows x K) in one go.  Lane (j, q) (j = lane % 16,
+// q = lane / 16) holds channels 16 q + 8 u .. 16 q + 8 u + 7 of a chunk for
+// product u of it (u = 0, 1).
+constexpr int kDecWaves = 16;
+constexpr int kDecAhead = 4;
+typedef float f32x4_t __attribute__((__vector_size__(16)));
+
+__global__ __launch_bounds__(kDecWaves * kWave) void oproj_mfma16_kernel(int n_tok, int width, int rank,
+                                                                          const uint16_t* __restrict__ x,
+                                                                          const uint16_t* __restrict__ w,
+                                                                          uint16_t* __restrict__ y) {
+  __shared__ float red[kDecWaves][2][4][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int j = lane & 15, q = lane >> 4;
+  const int r0 = blockIdx.y * 32, g = blockIdx.z;
+  const int n_groups = gridDim.z;
+  const int K = width / n_groups, nchunk = K / 64;
+  // rows past the last token repeat it; their products are never stored
+  const uint16_t* xrow = x + int64_t(min(j, n_tok - 1)) * width + int64_t(g) * K + 16 * q;
+  const uint16_t* wrow0 = w + (int64_t(g) * rank + r0 + j) * K + 16 * q;
+  const uint16_t* wrow1 = wrow0 + int64_t(16) * K;
+
+  f32x4_t acc[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[t][r] = 0.0f;
+  for (int c0 = wv; c0 < nchunk; c0 += kDecAhead * kDecWaves) {
+    uint4 a[kDecAhead][2], b[kDecAhead][2][2];
+#pragma unroll
+    for (int k = 0; k < kDecAhead; ++k) {
+      const int c = min(c0 + k * kDecWaves, nchunk - 1);  // unconditional: exact wait counts
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        a[k][u] = *reinterpret_cast<const uint4*>(xrow + 64 * c + 8 * u);
+        b[k][0][u] = *reinterpret_cast<const uint4*>(wrow0 + 64 * c + 8 * u);
+        b[k][1][u] = *reinterpret_cast<const uint4*>(wrow1 + 64 * c + 8 * u);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < kDecAhead; ++k) {
+      const uint32_t keep = c0 + k * kDecWaves < nchunk ? ~0u : 0u;  // zero for a chunk past the wave's range
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const uint4 av = {a[k][u].x & keep, a[k][u].y & keep, a[k][u].z & keep, a[k][u].w & keep};
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(b[k][t][u]), acc[t], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wv][t][r][lane] = acc[t][r];
+  __syncthreads();
+  // product element r of lane l: row 4 (l / 16) + r, column l % 16
+  const int o = threadIdx.x;
+  if (o < 512) {
+    const int t = o >> 8, r = (o >> 6) & 3, l = o & 63;
     float s = 0.0f;
 #pragma unroll
-    for (int v = 0; v < kOpWaves; ++v) s += red[((v * NT + t) * 16 + r) * 64 + l];
-    // product element r of lane l: row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
-    const int row = 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
-    const int tok = t0 + row;
-    if (tok < n_tok) y[int64_t(tok) * out_w + int64_t(g) * rank + r0 + 32 * t + (l & 31)] = f32_to_bf16(s);
+    for (int v = 0; v < kDecWaves; ++v) s += red[v][t][r][l];
+    const int tok = 4 * (l >> 4) + r;
+    if (tok < n_tok) y[int64_t(tok) * n_groups * rank + int64_t(g) * rank + r0 + 16 * t + (l & 15)] = f32_to_bf16(s);
   }
 }
 
@@ -140,7 +230,8 @@ __global__ __launch_bounds__(256) void oproj_generic_kernel(int n_tok, int width
     static_cast<float*>(y)[o] = s;
 }
 
-constexpr size_t oproj_lds(int nt) { return sizeof(float) * kOpWaves * nt * 16 * 64; }
+constexpr int kSplitWaves = 16;
+constexpr size_t kSplitLds = sizeof(float) * kSplitWaves * 16 * 64;  // 64 KB
 
 }  // namespace
 
@@ -149,18 +240,22 @@ hipError_t launch_oproj(int32_t act_dtype, int32_t n_tok, int32_t width, int32_t
   if (n_tok == 0) return hipSuccess;
   const int64_t K = width / n_groups;
   if (act_dtype == CSA2_BF16 && K % 64 == 0 && rank % 32 == 0) {
-    // two output tiles per wave once one-tile workgroups would fill the chip several times over
-    const int64_t tok_tiles = (n_tok + 31) / 32;
-    const bool two = rank % 64 == 0 && tok_tiles * (rank / 32) * n_groups >= 4 * 256;
-    const dim3 grid(uint32_t(tok_tiles), uint32_t(rank / (two ? 64 : 32)), uint32_t(n_groups));
     const auto* xb = static_cast<const uint16_t*>(x);
     const auto* wb = static_cast<const uint16_t*>(w);
     auto* yb = static_cast<uint16_t*>(y);
-    if (two)
-      return launch_kernel(CSA2_KERNEL_OPROJ_MFMA, oproj_mfma_kernel<2>, grid, dim3(kOpThreads), oproj_lds(2), stream,
+    // the 128 x 128 tiles once they cover the chip; else the K split
+    const int64_t big_tiles = (int64_t(n_tok) + 127) / 128 * (rank / 128) * n_groups;
+    if (rank % 128 == 0 && big_tiles >= 256) {
+      const dim3 grid(uint32_t((n_tok + 127) / 128), uint32_t(rank / 128), uint32_t(n_groups));
+      return launch_kernel(CSA2_KERNEL_OPROJ_MFMA, oproj_mfma_kernel<2, 8, false>, grid, dim3(8 * kWave), 0, stream,
                            int(n_tok), int(width), int(rank), xb, wb, yb);
-    return launch_kernel(CSA2_KERNEL_OPROJ_MFMA, oproj_mfma_kernel<1>, grid, dim3(kOpThreads), oproj_lds(1), stream,
-                         int(n_tok), int(width), int(rank), xb, wb, yb);
+    }
+    if (n_tok <= 16)
+      return launch_kernel(CSA2_KERNEL_OPROJ_MFMA16, oproj_mfma16_kernel, dim3(1, uint32_t(rank / 32), uint32_t(n_groups)),
+                           dim3(kDecWaves * kWave), 0, stream, int(n_tok), int(width), int(rank), xb, wb, yb);
+    const dim3 grid(uint32_t((n_tok + 31) / 32), uint32_t(rank / 32), uint32_t(n_groups));
+    return launch_kernel(CSA2_KERNEL_OPROJ_MFMA, oproj_mfma_kernel<1, kSplitWaves, true>, grid,
+                         dim3(kSplitWaves * kWave), kSplitLds, stream, int(n_tok), int(width), int(rank), xb, wb, yb);
   }
   const int64_t total = int64_t(n_tok) * n_groups * rank;
   return launch_kernel(CSA2_KERNEL_OPROJ_GENERIC, oproj_generic_kernel, dim3(uint32_t((total + 255) / 256)), dim3(256),

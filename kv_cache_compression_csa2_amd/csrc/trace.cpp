@@ -132,6 +132,7 @@ const char* csa2_kernel_name(int32_t kernel) {
     case CSA2_KERNEL_SCAN_PREFILL: return "scan_prefill_kernel";
     case CSA2_KERNEL_OPROJ_MFMA: return "oproj_mfma_kernel";
     case CSA2_KERNEL_OPROJ_GENERIC: return "oproj_generic_kernel";
+    case CSA2_KERNEL_OPROJ_MFMA16: return "oproj_mfma16_kernel";
     default: return "unknown";
   }
 }

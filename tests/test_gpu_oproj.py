@@ -25,6 +25,9 @@ CASES = [
     (5, 96, 3, 20, "f32", None),  # plain kernel, float32
     (3, 96, 3, 32, "bf16", None),  # K 32: plain kernel in bf16
     (7, 512, 1, 64, "bf16", None),  # one group
+    (1, 4096, 8, 32, "bf16", None),  # one token
+    (9, 10240, 2, 64, "bf16", None),  # K 5120: waves past 4 chunks loop again, with masked tails
+    (17, 4096, 4, 64, "bf16", None),  # just past the 16-token kernel
 ]
 
 
