@@ -321,9 +321,10 @@ typedef enum csa2_kernel {
   CSA2_KERNEL_ATTN_MERGE = 9,     /* attn_merge_kernel */
   CSA2_KERNEL_ATTN_FP4_G16 = 10,  /* attn_mfma_kernel over an FP4 cache, scales per 16 */
   CSA2_KERNEL_SCAN_PREFILL = 11,  /* scan_prefill_kernel (many queries per sequence) */
-  CSA2_KERNEL_OPROJ_MFMA = 12,    /* oproj_mfma_kernel (bf16 grouped output projection, > 16 rows) */
+  CSA2_KERNEL_OPROJ_MFMA = 12,    /* oproj_mfma_kernel (bf16 grouped output projection, K split) */
   CSA2_KERNEL_OPROJ_GENERIC = 13, /* oproj_generic_kernel */
-  CSA2_KERNEL_OPROJ_MFMA16 = 14   /* oproj_mfma16_kernel (bf16 grouped output projection, <= 16 rows) */
+  CSA2_KERNEL_OPROJ_MFMA16 = 14,  /* oproj_mfma16_kernel (bf16 grouped output projection, <= 16 rows) */
+  CSA2_KERNEL_OPROJ_LDS = 15      /* oproj_lds_kernel (bf16 grouped output projection, 128 x 128 tiles) */
 } csa2_kernel;
 
 typedef struct csa2_trace_record {

@@ -9,17 +9,12 @@
 // with float32 accumulation, stored in the activation type (bf16: round to
 // nearest even).
 //
-// The bf16 kernel is a matrix-core contraction in two layouts.  Few tokens
-// (decode): a workgroup computes 32 tokens x 32 outputs of one group, its 16
-// waves split the group's K channels into 64-channel chunks (wave w takes
-// chunks w, w + 16, ...) and their partial tiles are summed through LDS; the
-// kernel streams the 8 x 1024 x 4096 weights once, so it is HBM-bound, and
-// the split keeps 16 waves of loads in flight per compute unit.  Many tokens:
-// a workgroup computes 128 tokens x 128 outputs, its 8 waves as 4 x 2 tiles
-// of 32 x 64 over the whole K, so each token row and weight row a workgroup
-// reads serves 2 or 4 waves (through L1) and no reduction is needed.  Either
-// way each lane reads 64 contiguous bytes of a token row and of each weight
-// row per chunk.
+// The bf16 path runs on the matrix cores in three kernels: at most 16 rows
+// (decode) oproj_mfma16_kernel streams the 8 x 1024 x 4096 weights once
+// (HBM-bound); many rows, with 128-output tiles, oproj_lds_kernel stages
+// 128 x 128 tiles through LDS (matrix-bound); other shapes take
+// oproj_mfma_kernel, whose 16 waves split K over one 32 x 32 tile.  Each is
+// described at its definition.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -28,7 +23,6 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(16)));
 typedef float f32x16_t __attribute__((__vector_size__(64)));
-
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
@@ -42,23 +36,21 @@ struct OpChunk {
   uint4 b[NT][4];
 };
 
-// NT: 32-output tiles per wave.  SPLITK: WAVES waves share one 32 x NT*32
-// tile and split K; else WAVES = 8 waves tile 128 tokens x 64 NT outputs.
-template <int NT, int WAVES, bool SPLITK>
+// NT: 32-output tiles per wave; the WAVES waves share one 32 x NT*32 tile
+// and split K.
+template <int NT, int WAVES>
 __global__ __launch_bounds__(WAVES * kWave) void oproj_mfma_kernel(int n_tok, int width, int rank,
                                                                    const uint16_t* __restrict__ x,
                                                                    const uint16_t* __restrict__ w,
                                                                    uint16_t* __restrict__ y) {
-  static_assert(SPLITK || WAVES == 8, "the tiled layout is 4 x 2 waves");
-  extern __shared__ float red[];  // SPLITK: [WAVES][NT][16][64]
+  extern __shared__ float red[];  // [WAVES][NT][16][64]
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int i = lane & 31, h = lane >> 5;
   const int g = blockIdx.z;
-  const int t0 = SPLITK ? blockIdx.x * 32 : blockIdx.x * 128 + 32 * (wv & 3);
-  const int r0 = SPLITK ? blockIdx.y * 32 * NT : blockIdx.y * 64 * NT + 32 * NT * (wv >> 2);
+  const int t0 = blockIdx.x * 32, r0 = blockIdx.y * 32 * NT;
   const int n_groups = gridDim.z;
   const int K = width / n_groups, nchunk = K / 64;
-  const int c_first = SPLITK ? wv : 0, c_step = SPLITK ? WAVES : 1;
+  const int c_first = wv, c_step = WAVES;
 
   // rows past the last token repeat it; their products are never stored
   const uint16_t* xrow = x + int64_t(min(t0 + i, n_tok - 1)) * width + int64_t(g) * K + 32 * h;
@@ -109,31 +101,22 @@ __global__ __launch_bounds__(WAVES * kWave) void oproj_mfma_kernel(int n_tok, in
     contract(b1, c + c_step < nchunk ? ~0u : 0u);
   }
 
-  // product element r of lane l: row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
+  // partial tiles of the waves, summed through LDS (lane-contiguous: no bank
+  // conflicts); product element r of lane l: row 8 (r / 4) + 4 (l / 32) +
+  // r % 4, column l % 32
   const int out_w = n_groups * rank;
-  if constexpr (!SPLITK) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int tok = t0 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (tok < n_tok) y[int64_t(tok) * out_w + int64_t(g) * rank + r0 + 32 * t + i] = f32_to_bf16(acc[t][r]);
-      }
-  } else {
-    // partial tiles of the waves, summed through LDS (lane-contiguous: no bank conflicts)
+    for (int r = 0; r < 16; ++r) red[((wv * NT + t) * 16 + r) * 64 + lane] = acc[t][r];
+  __syncthreads();
+  for (int o = threadIdx.x; o < NT * 1024; o += WAVES * kWave) {
+    const int t = o >> 10, r = (o >> 6) & 15, l = o & 63;
+    float s = 0.0f;
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) red[((wv * NT + t) * 16 + r) * 64 + lane] = acc[t][r];
-    __syncthreads();
-    for (int o = threadIdx.x; o < NT * 1024; o += WAVES * kWave) {
-      const int t = o >> 10, r = (o >> 6) & 15, l = o & 63;
-      float s = 0.0f;
-#pragma unroll
-      for (int v = 0; v < WAVES; ++v) s += red[((v * NT + t) * 16 + r) * 64 + l];
-      const int tok = t0 + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
-      if (tok < n_tok) y[int64_t(tok) * out_w + int64_t(g) * rank + r0 + 32 * t + (l & 31)] = f32_to_bf16(s);
-    }
+    for (int v = 0; v < WAVES; ++v) s += red[((v * NT + t) * 16 + r) * 64 + l];
+    const int tok = t0 + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+    if (tok < n_tok) y[int64_t(tok) * out_w + int64_t(g) * rank + r0 + 32 * t + (l & 31)] = f32_to_bf16(s);
   }
 }
 
@@ -210,6 +193,116 @@ __global__ __launch_bounds__(kDecWaves * kWave) void oproj_mfma16_kernel(int n_t
   }
 }
 
+// Many tokens (prefill): a workgroup computes 128 tokens x 128 outputs of one
+// group with 4 waves of 64 x 64 (2 x 2 products of 32 x 32 each).  The
+// 64-channel slices of its 128 token rows and 128 weight rows are copied
+// global -> LDS (global_load_lds_dwordx4: no registers, and from inline
+// assembly, so the compiler neither drains nor moves them) a slice ahead into
+// the other of two 32 KB stages; each wave issues 8 of a slice's 32 one-KB
+// copies, so one s_waitcnt vmcnt(8) and a barrier make a slice ready.  Each
+// 128-byte LDS row holds its eight 16-byte chunks XOR-swizzled by (row / 2)
+// % 8, so a copy instruction still reads 8 whole rows (coalesced) and the
+// operand reads of 16 consecutive rows fall on distinct bank groups.  Each
+// token and weight row is fetched once per workgroup and read by two waves
+// from LDS: 64 flop per byte fetched.
+constexpr int kTile = 128;
+constexpr uint32_t kStageBytes = 2 * kTile * 128;  // A rows then B rows: 32 KB
+constexpr size_t kLdsTileBytes = 2 * kStageBytes;  // two stages: 64 KB
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; naming it tells the compiler it changes
+// Copy 16 bytes per lane from global `src` to LDS byte address `lds_addr` +
+// 16 * lane.  Completion is tracked only by the caller's s_waitcnt vmcnt.
+__device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr), "v"(src) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// byte offset of 16-byte chunk c (0..7) of LDS row r inside a stage region
+__device__ __forceinline__ uint32_t tile_off(int r, int c) { return uint32_t(r * 128 + 16 * (c ^ ((r >> 1) & 7))); }
+
+__global__ __launch_bounds__(256, 2) void oproj_lds_kernel(int n_tok, int width, int rank,
+                                                             const uint16_t* __restrict__ x,
+                                                             const uint16_t* __restrict__ w,
+                                                             uint16_t* __restrict__ y) {
+  extern __shared__ __align__(16) uint8_t tile[];  // [2 stages][A 128 rows | B 128 rows][128 bytes]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int i = lane & 31, h = lane >> 5;
+  const int wm = wv & 1, wn = wv >> 1;
+  const int t0 = blockIdx.x * kTile, r0 = blockIdx.y * kTile, g = blockIdx.z;
+  const int n_groups = gridDim.z;
+  const int K = width / n_groups, nchunk = K / 64;
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
+      uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)tile)));
+
+  // copy m (0..31) of a slice: rows 8 (m % 16) .. + 7 of A (m < 16) or B;
+  // lane l fills physical chunk l % 8 of row 8 (m % 16) + l / 8
+  auto issue = [&](int c, int stage) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int m = 8 * wv + j;
+      const int r = 8 * (m & 15) + (lane >> 3);
+      const int ch = (lane & 7) ^ ((r >> 1) & 7);  // the logical chunk that lands there
+      const uint16_t* src = m < 16
+          ? x + int64_t(min(t0 + r, n_tok - 1)) * width + int64_t(g) * K + 64 * c + 8 * ch  // rows past the last token repeat it
+          : w + (int64_t(g) * rank + r0 + r) * K + 64 * c + 8 * ch;
+      copy16_to_lds(src, lds0 + stage * kStageBytes + m * 1024);
+    }
+  };
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+
+  issue(0, 0);
+  for (int c = 0; c < nchunk; ++c) {
+    // the other stage was last read before the previous iteration's closing
+    // barrier; the last slice is copied again into it, unused
+    issue(min(c + 1, nchunk - 1), (c + 1) & 1);
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // this wave's copies of slice c have landed
+    __syncthreads();                                   // and every wave's
+    const uint8_t* st = tile + (c & 1) * kStageBytes;
+    // lane (i, h): logical chunk 2 k + h (channels 16 k + 8 h .. + 7) of its rows
+    bf16x8_t av[4][2], bv[4][2];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+        av[k][a] = *reinterpret_cast<const bf16x8_t*>(st + tile_off(64 * wm + 32 * a + i, 2 * k + h));
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        bv[k][b] = *reinterpret_cast<const bf16x8_t*>(st + kStageBytes / 2 + tile_off(64 * wn + 32 * b + i, 2 * k + h));
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[k][a], bv[k][b], acc[a][b], 0, 0, 0);
+    __syncthreads();  // stage c & 1 is free for the next iteration's copies
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no copy may land after the workgroup ends
+
+  // product element r of lane l: row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
+  const int out_w = n_groups * rank;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int tok = t0 + 64 * wm + 32 * a + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (tok < n_tok)
+          y[int64_t(tok) * out_w + int64_t(g) * rank + r0 + 64 * wn + 32 * b + i] = f32_to_bf16(acc[a][b][r]);
+      }
+}
+
 // Any shape and either activation type: one thread per output, float32
 // accumulation in channel order.
 __global__ __launch_bounds__(256) void oproj_generic_kernel(int n_tok, int width, int n_groups, int rank, int act_bf16,
@@ -246,15 +339,22 @@ hipError_t launch_oproj(int32_t act_dtype, int32_t n_tok, int32_t width, int32_t
     // the 128 x 128 tiles once they cover the chip; else the K split
     const int64_t big_tiles = (int64_t(n_tok) + 127) / 128 * (rank / 128) * n_groups;
     if (rank % 128 == 0 && big_tiles >= 256) {
+      static bool attr_set = false;
+      if (!attr_set) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(oproj_lds_kernel),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(kLdsTileBytes));
+        if (e != hipSuccess) return e;
+        attr_set = true;
+      }
       const dim3 grid(uint32_t((n_tok + 127) / 128), uint32_t(rank / 128), uint32_t(n_groups));
-      return launch_kernel(CSA2_KERNEL_OPROJ_MFMA, oproj_mfma_kernel<2, 8, false>, grid, dim3(8 * kWave), 0, stream,
-                           int(n_tok), int(width), int(rank), xb, wb, yb);
+      return launch_kernel(CSA2_KERNEL_OPROJ_LDS, oproj_lds_kernel, grid, dim3(256), kLdsTileBytes, stream, int(n_tok),
+                           int(width), int(rank), xb, wb, yb);
     }
     if (n_tok <= 16)
       return launch_kernel(CSA2_KERNEL_OPROJ_MFMA16, oproj_mfma16_kernel, dim3(1, uint32_t(rank / 32), uint32_t(n_groups)),
                            dim3(kDecWaves * kWave), 0, stream, int(n_tok), int(width), int(rank), xb, wb, yb);
     const dim3 grid(uint32_t((n_tok + 31) / 32), uint32_t(rank / 32), uint32_t(n_groups));
-    return launch_kernel(CSA2_KERNEL_OPROJ_MFMA, oproj_mfma_kernel<1, kSplitWaves, true>, grid,
+    return launch_kernel(CSA2_KERNEL_OPROJ_MFMA, oproj_mfma_kernel<1, kSplitWaves>, grid,
                          dim3(kSplitWaves * kWave), kSplitLds, stream, int(n_tok), int(width), int(rank), xb, wb, yb);
   }
   const int64_t total = int64_t(n_tok) * n_groups * rank;

@@ -133,6 +133,7 @@ const char* csa2_kernel_name(int32_t kernel) {
     case CSA2_KERNEL_OPROJ_MFMA: return "oproj_mfma_kernel";
     case CSA2_KERNEL_OPROJ_GENERIC: return "oproj_generic_kernel";
     case CSA2_KERNEL_OPROJ_MFMA16: return "oproj_mfma16_kernel";
+    case CSA2_KERNEL_OPROJ_LDS: return "oproj_lds_kernel";
     default: return "unknown";
   }
 }

@@ -28,6 +28,8 @@ CASES = [
     (1, 4096, 8, 32, "bf16", None),  # one token
     (9, 10240, 2, 64, "bf16", None),  # K 5120: waves past 4 chunks loop again, with masked tails
     (17, 4096, 4, 64, "bf16", None),  # just past the 16-token kernel
+    (1000, 1024, 8, 512, "bf16", None),  # 128 x 128 LDS tiles, ragged last token tile
+    (500, 1536, 8, 1024, "bf16", None),  # LDS tiles with an odd number of 64-channel slices
 ]
 
 
