@@ -235,8 +235,12 @@ __device__ int select_top_impl(const SelLds L, int n, int m, lds_u32* out) {
 // kBins bins, which cut the atomic collisions of clustered keys; fine bins
 // measured slower there (a threshold in the dense middle, or 2048 clustered
 // pool maxima, still needs a second pass).
+// The register count follows the level's size (4, 8 or 16 keys per thread):
+// a loop over 16 registers holding 4 keys would do 4x the work per pass.
 __device__ __attribute__((noinline)) int select_top(const SelLds L, int n, int m, lds_u32* out) {
-  if (n > 2048 && n <= 4096 && 4 * m <= n) return select_top_impl<true, kMaxCand / kNT>(L, n, m, out);
+  if (n > 2048 && n <= 4096 && 4 * m <= n) return select_top_impl<true, 4>(L, n, m, out);
+  if (n <= 4 * kNT) return select_top_impl<false, 4>(L, n, m, out);
+  if (n <= 8 * kNT) return select_top_impl<false, 8>(L, n, m, out);
   return select_top_impl<false, kMaxCand / kNT>(L, n, m, out);
 }
 // The same, inlined: the 64-register variant of the kernel must not call a
