@@ -123,7 +123,11 @@ __device__ int select_top_impl(const SelLds L, int n, int m, lds_u32* out) {
   uint32_t T = kKeyNegInf, need = 0;
   if (total > uint32_t(m)) {
     need = uint32_t(m);
-    for (;;) {
+    // the found bin goes to misc[0..2] on even passes and misc[4..6] on odd
+    // ones, so no barrier is needed between reading it and the next pass
+    // (a slot is rewritten two passes later, after two more barriers)
+    for (int pass = 0;; ++pass) {
+      lds_u32* const found = L.misc + 4 * (pass & 1);
       const uint64_t width = uint64_t(hi) - lo + 1;
       const int bits = 64 - __clzll(width - 1);  // bits spanned by the interval
       const int shift = bits > bin_bits ? bits - bin_bits : 0;
@@ -171,17 +175,16 @@ __device__ int select_top_impl(const SelLds L, int n, int m, lds_u32* out) {
 #pragma unroll
         for (int i = nb - 1; i >= 0; --i) {
           if (need > above && need <= above + hb[i]) {
-            L.misc[0] = uint32_t(b0 + i);
-            L.misc[1] = need - above;
-            L.misc[2] = hb[i];
+            found[0] = uint32_t(b0 + i);
+            found[1] = need - above;
+            found[2] = hb[i];
           }
           above += hb[i];
         }
       }
       __syncthreads();
-      const uint32_t bin = L.misc[0], in_bin = L.misc[2];
-      need = L.misc[1];
-      __syncthreads();
+      const uint32_t bin = found[0], in_bin = found[2];
+      need = found[1];
       const uint64_t new_lo = uint64_t(lo) + (uint64_t(bin) << shift);
       hi = uint32_t(min(uint64_t(hi), new_lo + (uint64_t(1) << shift) - 1));
       lo = uint32_t(new_lo);
