@@ -118,7 +118,9 @@ __device__ int select_top_impl(const SelLds L, int n, int m, lds_u32* out) {
 
   const uint32_t total = reduce_waves(L, 0, 0);
   uint32_t lo = reduce_waves(L, kNW, 1), hi = reduce_waves(L, 2 * kNW, 2);
-  __syncthreads();
+  // wred is next written by the compaction, or by a pass after its histogram
+  // barrier: only the first case needs a barrier here (total is uniform)
+  if (total <= uint32_t(m)) __syncthreads();
 
   uint32_t T = kKeyNegInf, need = 0;
   if (total > uint32_t(m)) {
