@@ -8,10 +8,12 @@ Every tensor gets its own PCG64 stream, keyed by (seed, workload, tensor,
 layer, sequence, chunk), so a test can regenerate one sequence or one chunk
 of a long latent without drawing the rest.
 
-Distributions (one reading of the workload descriptions):
-latent, queries, indexer queries, head weights, compressor logits and window
-rows are N(0, 1); the indexer-K projection W_ik is N(0, 1/d) (standard
-deviation 1/sqrt(fan_in)).
+Distributions (the pages give none; the plainest choice for trained
+activations at unit scale): latent, queries, indexer queries, head weights,
+compressor logits and window rows are N(0, 1); the indexer-K projection W_ik
+is N(0, 1/d) (standard deviation 1/sqrt(fan_in)); FP8 window rows are drawn
+as E4M3 code bytes; the output projection's inputs are described at
+oproj_inputs.
 """
 from __future__ import annotations
 
