@@ -309,7 +309,7 @@ def main() -> int:
                     help="after the run, copy a buffer of this many MiB 5 times (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (use --gpus 1)", file=sys.stderr)
         return 2
 
     if args.oproj_tokens:
