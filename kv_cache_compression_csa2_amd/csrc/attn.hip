@@ -45,7 +45,8 @@ __global__ __launch_bounds__(kThreads) void attn_generic_kernel(
   __syncthreads();
 
   const int64_t win0 = t - window + 1 > 0 ? t - window + 1 : 0;
-  const int64_t sfirst = swa_first[b];
+  // no window buffer (n_swa == 0): swa_first may be NULL and no window row is read
+  const int64_t sfirst = (swa && n_swa > 0) ? swa_first[b] : 0;
   const int n_rows = topk + window;
   const float scale = rope.logit_scale;
 

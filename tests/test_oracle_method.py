@@ -11,6 +11,7 @@ from scipy.special import logsumexp
 from oracle import csa2, driver, footprint, formats
 
 import synth
+from dataclasses import replace
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -120,6 +121,21 @@ def test_rope_matches_complex_rotation_and_is_relative():
     assert abs(a - b) < 1e-9
 
 
+def test_rope_frequencies_hand_worked():
+    """Rotation angles worked by hand for theta = 10000: with 4 rotary
+    channels pair 0 turns 1 rad per position and pair 1 turns
+    10000^(-1/2) = 0.01 rad, so at position 100 the pairs have turned 100 rad
+    and exactly 1 rad; with 8 rotary channels pair 2 turns 10000^(-1/2) too."""
+    x = np.array([5.0, 1.0, 0.0, 1.0, 0.0])  # one non-rotary channel, then pairs (1, 0), (1, 0)
+    y = csa2.rope(x, 100, 4, 10000.0)
+    assert y[0] == 5.0
+    assert np.allclose(y[1:3], [np.cos(100.0), np.sin(100.0)], atol=1e-12)
+    assert np.allclose(y[3:5], [np.cos(1.0), np.sin(1.0)], atol=1e-12)
+    z = csa2.rope(np.array([1.0, 0.0] * 4), 100, 8, 10000.0)
+    assert np.allclose(z[4:6], [np.cos(1.0), np.sin(1.0)], atol=1e-12)
+    assert np.allclose(z[2:4], [np.cos(10.0), np.sin(10.0)], atol=1e-12)  # 10000^(-1/4) = 0.1 rad per position
+
+
 # ------------------------------------------------------------------- scores --
 
 
@@ -136,6 +152,26 @@ def test_indexer_score_invariants():
     assert np.allclose(one, torch.relu(torch.from_numpy(K) @ torch.from_numpy(q[0])).numpy())
     # negated query on every head: scores of heads with all-negative dots vanish
     assert np.all(csa2.indexer_scores(-np.abs(q), np.ones(4), np.abs(K)) == 0)
+
+
+def test_indexer_score_relu_is_per_head_hand_worked():
+    """Two heads whose dot products have opposite signs separate a ReLU taken
+    per head from one taken after the weighted head sum (the reading of the
+    zartbot walkthrough, 2.3.1: each head's score is clipped at zero before
+    the query's head weights combine them).  Values worked by hand."""
+    K = np.array([[1.0, 0.0], [0.0, 1.0]])  # entry 0 = e0, entry 1 = e1
+    q = np.array([[2.0, 0.0], [-3.0, 0.0]])  # head 0 . e0 = +2, head 1 . e0 = -3; both 0 on e1
+    # w = (1, 1): per head 1*2 + 1*0 = 2 (after the sum it would be max(0, -1) = 0)
+    assert list(csa2.indexer_scores(q, np.array([1.0, 1.0]), K)) == [2.0, 0.0]
+    # w = (1, -1): the negative weight meets a clipped head, so it adds nothing:
+    # 1*2 + (-1)*0 = 2 (after the sum: max(0, 2 + 3) = 5)
+    assert list(csa2.indexer_scores(q, np.array([1.0, -1.0]), K)) == [2.0, 0.0]
+    # w = (-1, 1): a negative weight on the positive head makes the score negative,
+    # -2 + 0 = -2 (after the sum it could never fall below 0)
+    assert list(csa2.indexer_scores(q, np.array([-1.0, 1.0]), K)) == [-2.0, 0.0]
+    # three heads, integer arithmetic: dots (4, -1, 3), w (0.5, 7, -2) -> 2 + 0 - 6 = -4
+    q3 = np.array([[4.0, 0.0], [-1.0, 0.0], [3.0, 0.0]])
+    assert csa2.indexer_scores(q3, np.array([0.5, 7.0, -2.0]), K[:1])[0] == -4.0
 
 
 # -------------------------------------------------------------------- top-k --
@@ -327,3 +363,38 @@ def test_yarn_rotation_is_relative_and_norm_preserving():
 def test_yarn_temperature_grows_with_the_factor():
     ts = [csa2.logit_temperature(csa2.Rope(10000.0, s, 65536)) for s in (1.0, 2.0, 4.0, 16.0, 64.0)]
     assert ts[0] == 1.0 and all(b > a for a, b in zip(ts, ts[1:]))
+
+
+# ------------------------------------------------------------ lazy cache --
+
+
+def _lazy_matches_built(wl, ids):
+    inp = synth.Inputs(wl)
+    built = driver.build_cache(inp, 0, wl.context)
+    lazy = driver.LazyMainCache(inp, 0, wl.context)
+    assert lazy.n_entries == built.n_entries == wl.capacity
+    for key, arr in built.idx_raw.items():  # the whole indexer K, byte for byte
+        assert np.array_equal(lazy.idx_raw[key], arr), key
+    ids = np.asarray(ids, dtype=np.int64)
+    rows = lazy.main_raw_rows(ids)
+    assert set(rows) == set(built.main_raw)
+    for key, arr in built.main_raw.items():  # main-KV rows made on demand
+        assert np.array_equal(rows[key], arr[ids]), key
+    assert np.array_equal(lazy.main_rows(ids), built.main_rows(ids))
+
+
+def test_lazy_main_cache_equals_built_cache_ratio2():
+    """The deferred main-KV rows and the indexer K of LazyMainCache are the
+    bytes build_cache stores, at ratio 2, on both sides of the 4096-position
+    latent fetches (entries 2047/2048, 4095/4096) and of the 16384-position
+    build chunks (entries 8191/8192), first and last entries included."""
+    wl = replace(synth.get("tiny_encoder"), name="lazy_ratio2", prior=2 * 8300, new=0, n_q=1)
+    _lazy_matches_built(wl, [0, 1, 2047, 2048, 2049, 4095, 4096, 8191, 8192, 8193, wl.capacity - 1, 5, 4096])
+
+
+def test_lazy_main_cache_equals_built_cache_fp4_pages():
+    """The same in the pages' FP4 format (main KV one E4M3 scale per 16
+    channels, indexer K per 32) at ratio 1, across the 4096-entry fetch and
+    the 16384-entry build chunk."""
+    wl = replace(synth.get("fp4_pages"), name="lazy_fp4_pages", batch=1, prior=16400, new=1, n_q=1)
+    _lazy_matches_built(wl, [0, 4095, 4096, 8191, 8192, 12288, 16383, 16384, 16385, wl.capacity - 1])
