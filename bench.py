@@ -20,7 +20,12 @@ flops per launch for prefill (many queries share each sequence's K).
 
 Prints one JSON line: whole-step tokens/s, the per-kernel device times, the
 scan roofline, and the float64 CPU oracle timed on a bounded sample of the
-same workload on the host cores.
+same workload on the host cores (all BLAS threads, then one).  Each extra
+workload (--extra, default fp4_1m: 2 x 1M context with FP4 KV) is timed the
+same way in the same run and reported as an object of that line.  Decode
+rooflines carry two denominators: the published 8 TB/s HBM peak and the
+rate the library's streaming-read probe measures for a working set of the
+scan's size on this GPU.
 """
 from __future__ import annotations
 
@@ -257,7 +262,47 @@ def run_oproj(n_tok: int, steps: int, warmup: int, copies: int) -> dict:
             "roofline": roof, "cpu_baseline": None}
 
 
-def cpu_baseline(wl, seconds: float) -> dict:
+def read_ceiling(nbytes: float, copies: int = 4, reps: int = 20) -> dict:
+    """Measured streaming-read rate for a working set of `nbytes`: the
+    library's read probe over `copies` rotated buffers of that size (so the
+    Infinity Cache cannot hold the one being read), mean device time from the
+    kernel trace."""
+    import torch
+
+    from kv_cache_compression_csa2_amd import binding as B
+
+    n = int(nbytes) // 16 * 16
+    bufs = [torch.ones(n, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    for i in range(copies):
+        B.csa2_read_probe(bufs[i], n, sink)
+    torch.cuda.synchronize()
+    B.csa2_trace_enable(reps)
+    for i in range(reps):
+        B.csa2_read_probe(bufs[i % copies], n, sink)
+    torch.cuda.synchronize()
+    recs, dropped = B.csa2_trace_read(reps)
+    B.csa2_trace_enable(0)
+    if dropped or len(recs) != reps:
+        raise RuntimeError(f"read probe trace incomplete: {len(recs)} records, {dropped} dropped")
+    ms = sum(r[1] for r in recs) / reps
+    return {"bytes": n, "ms": round(ms, 5), "gbps": round(n / (ms * 1e-3) / 1e9, 1), "copies": copies}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(wl, seconds: float, single_thread_seconds: float = 0.0) -> dict:
     """The float64 oracle timed on the host cores on a sample of the workload's sequences."""
     import numpy as np
     from threadpoolctl import threadpool_info
@@ -275,22 +320,81 @@ def cpu_baseline(wl, seconds: float) -> dict:
     logits, w_ik = inp.pair_logits(), inp.w_ik()
     q_pos = wl.q_positions()[seqs]
     n_entries = [c.n_entries for c in caches]
-    done = 0
-    t0 = time.perf_counter()
-    while True:
-        for i in range(len(seqs)):
-            if wl.new:
-                oc.make_entries(new_lat[i], wl.prior, logits, w_ik, wl.ratio, wl.d_rope, driver.rope_cfg(wl), wl.kv,
-                                wl.main_group, wl.idx_group)
-        oc.run_group(dims, caches, n_entries, q_pos, specs)
-        done += len(seqs) * wl.n_q
-        if time.perf_counter() - t0 >= seconds:
-            break
-    el = time.perf_counter() - t0
+
+    def timed(limit):
+        done = 0
+        t0 = time.perf_counter()
+        while True:
+            for i in range(len(seqs)):
+                if wl.new:
+                    oc.make_entries(new_lat[i], wl.prior, logits, w_ik, wl.ratio, wl.d_rope, driver.rope_cfg(wl),
+                                    wl.kv, wl.main_group, wl.idx_group)
+            oc.run_group(dims, caches, n_entries, q_pos, specs)
+            done += len(seqs) * wl.n_q
+            if time.perf_counter() - t0 >= limit:
+                break
+        return done, time.perf_counter() - t0
+
+    done, el = timed(seconds)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    return {"value": done / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{wl.name}: sequences {seqs} of {wl.batch}, one decode step each, repeated "
-                      f"{done // max(1, len(seqs) * wl.n_q)} times in {el:.1f} s (cache build untimed)"}
+    out = {"value": done / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{wl.name}: sequences {seqs} of {wl.batch}, one decode step each, repeated "
+                     f"{done // max(1, len(seqs) * wl.n_q)} times in {el:.1f} s (cache build untimed)",
+           "cpu_model": cpu_model(), "affinity_cores": len(os.sched_getaffinity(0))}
+    if single_thread_seconds > 0:
+        from threadpoolctl import threadpool_limits
+
+        with threadpool_limits(limits=1):
+            d1, e1 = timed(single_thread_seconds)
+        out["single_thread_value"] = d1 / e1
+        out["single_thread_sample"] = f"the same step, BLAS limited to 1 thread, repeated {d1 // max(1, len(seqs) * wl.n_q)} times in {e1:.1f} s"
+    return out
+
+
+def measure(wl, args) -> dict:
+    """Time one workload's step (graph replays), its kernels (library trace),
+    the scan's roofline and the measured read ceiling at the scan's bytes."""
+    ms, launches = run_gpu(wl, args.steps, args.warmup, args.copies, not args.eager)
+    print(f"[bench] gpu done: {ms:.4f} ms/step; kernels (ms): "
+          + ", ".join(f"{k} {v:.4f}" for k, v in launches), file=sys.stderr, flush=True)
+    nbytes = algorithmic_bytes(wl)
+    tokens = wl.batch * wl.n_q
+    work = scan_work(wl)
+    scan_ms = next(v for k, v in launches if k.startswith("scan_"))
+    scan_name = next(k for k, v in launches if k.startswith("scan_"))
+    ceiling = None
+    if wl.n_q == 1:
+        ceiling = read_ceiling(work["bytes"], copies=args.copies)
+        print(f"[bench] read ceiling at {ceiling['bytes'] / 1e6:.1f} MB: {ceiling['gbps']:.0f} GB/s",
+              file=sys.stderr, flush=True)
+        achieved = work["bytes"] / (scan_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": scan_name, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "per_launch": work["bytes"],
+                "avg_ms": round(scan_ms, 5), "measured_peak": ceiling["gbps"],
+                "frac_of_measured": round(achieved / ceiling["gbps"], 4)}
+    else:
+        achieved = work["flops"] / (scan_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": scan_name, "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "per_launch": work["flops"],
+                "avg_ms": round(scan_ms, 5)}
+    roof["traffic"] = recorded_traffic(wl.name, scan_name)
+    step_gbps = nbytes["total"] / (ms * 1e-3) / 1e9
+    return {
+        "value": round(tokens / (ms * 1e-3), 1), "ms_per_step": round(ms, 5),
+        "dtype": wl.act if wl.kv != "fp4" else "bf16+fp4kv",
+        "config": {"workload": wl.name, "batch": wl.batch, "context": wl.context, "ratio": wl.ratio,
+                   "kv": wl.kv, "heads": f"{wl.n_heads}x{wl.d}", "indexer": f"{wl.n_idx_heads}x{wl.d_idx}",
+                   "topk": wl.topk, "window": wl.window, "window_rows": "fp8" if wl.swa == "fp8" else wl.act,
+                   "queries_per_seq": wl.n_q,
+                   "layers": [p.mode for p in wl.layers], "cache_copies": args.copies,
+                   "launch": "eager" if args.eager else "hip_graph"},
+        "step_hbm_gbps": round(step_gbps, 1),
+        "step_hbm_frac": round(step_gbps / HBM_PEAK_GBPS, 4),
+        "step_hbm_frac_of_measured": round(step_gbps / ceiling["gbps"], 4) if ceiling else None,
+        "step_bytes": nbytes["total"],
+        "kernels_ms": [[k, round(v, 5)] for k, v in launches],
+        "roofline": roof,
+    }
 
 
 def main() -> int:
@@ -303,6 +407,11 @@ def main() -> int:
     ap.add_argument("--eager", action="store_true", help="launch the timed steps directly instead of replaying HIP graphs")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-single-seconds", type=float, default=6.0,
+                    help="also time the oracle with BLAS limited to one thread (0 skips it)")
+    ap.add_argument("--extra", default="fp4_1m",
+                    help="comma-separated workloads timed after the main one and reported as objects of the "
+                         "same line ('none' for none)")
     ap.add_argument("--oproj-tokens", type=int, default=0,
                     help="time only the grouped output projection, for this many attention-output rows")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -321,9 +430,7 @@ def main() -> int:
 
     wl = synth.get(args.workload)
     print(f"[bench] {wl.name}: {wl.description}", file=sys.stderr, flush=True)
-    ms, launches = run_gpu(wl, args.steps, args.warmup, args.copies, not args.eager)
-    print(f"[bench] gpu done: {ms:.4f} ms/step; kernels (ms): "
-          + ", ".join(f"{k} {v:.4f}" for k, v in launches), file=sys.stderr, flush=True)
+    res = measure(wl, args)
     if args.copy_mib:
         import torch
 
@@ -333,45 +440,36 @@ def main() -> int:
         for _ in range(5):
             dst.copy_(src)
         torch.cuda.synchronize()
+        del src, dst
         print(f"[bench] copy calibration: 5 copies of {args.copy_mib} MiB", file=sys.stderr, flush=True)
 
-    nbytes = algorithmic_bytes(wl)
-    tokens = wl.batch * wl.n_q
-    work = scan_work(wl)
-    scan_ms = next(v for k, v in launches if k.startswith("scan_"))
-    scan_name = next(k for k, v in launches if k.startswith("scan_"))
-    if wl.n_q == 1:
-        achieved = work["bytes"] / (scan_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": scan_name, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "per_launch": work["bytes"],
-                "avg_ms": round(scan_ms, 5)}
-    else:
-        achieved = work["flops"] / (scan_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": scan_name, "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "per_launch": work["flops"],
-                "avg_ms": round(scan_ms, 5)}
-    roof["traffic"] = recorded_traffic(wl.name, scan_name)
+    extras = {}
+    for name in [x for x in args.extra.split(",") if x and x != "none" and x != wl.name]:
+        import torch
+
+        torch.cuda.empty_cache()
+        ewl = synth.get(name)
+        print(f"[bench] {ewl.name}: {ewl.description}", file=sys.stderr, flush=True)
+        r = measure(ewl, args)
+        extras[name] = {"value": r["value"], "unit": "tokens/s", "ms_per_step": r["ms_per_step"],
+                        "dtype": r["dtype"], "config": r["config"], "step_hbm_gbps": r["step_hbm_gbps"],
+                        "step_hbm_frac": r["step_hbm_frac"], "step_hbm_frac_of_measured": r["step_hbm_frac_of_measured"],
+                        "step_bytes": r["step_bytes"], "kernels_ms": r["kernels_ms"], "roofline": r["roofline"]}
+
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.cpu_seconds)
+        cpu = cpu_baseline(wl, args.cpu_seconds, args.cpu_single_seconds)
         print(f"[bench] cpu baseline done: {cpu['value']:.2f} tokens/s", file=sys.stderr, flush=True)
     out = {
-        "metric": METRIC, "value": round(tokens / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": wl.act if wl.kv != "fp4" else "bf16+fp4kv",
-        "data": "synthetic",
-        "config": {"workload": wl.name, "batch": wl.batch, "context": wl.context, "ratio": wl.ratio,
-                   "kv": wl.kv, "heads": f"{wl.n_heads}x{wl.d}", "indexer": f"{wl.n_idx_heads}x{wl.d_idx}",
-                   "topk": wl.topk, "window": wl.window, "window_rows": "fp8" if wl.swa == "fp8" else wl.act,
-                   "queries_per_seq": wl.n_q,
-                   "layers": [p.mode for p in wl.layers], "cache_copies": args.copies,
-                   "launch": "eager" if args.eager else "hip_graph"},
-        "step_hbm_gbps": round(nbytes["total"] / (ms * 1e-3) / 1e9, 1),
-        "step_hbm_frac": round(nbytes["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-        "step_bytes": nbytes["total"],
-        "kernels_ms": [[k, round(v, 5)] for k, v in launches],
-        "roofline": roof, "cpu_baseline": cpu,
+        "metric": METRIC, "value": res["value"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": res["dtype"], "data": "synthetic",
+        "config": res["config"],
+        "step_hbm_gbps": res["step_hbm_gbps"], "step_hbm_frac": res["step_hbm_frac"],
+        "step_hbm_frac_of_measured": res["step_hbm_frac_of_measured"], "step_bytes": res["step_bytes"],
+        "kernels_ms": res["kernels_ms"], "roofline": res["roofline"], "cpu_baseline": cpu,
     }
+    out.update(extras)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 3
+#define CSA2_ABI_VERSION 4
 
 typedef enum csa2_status {
   CSA2_OK = 0,
@@ -324,7 +324,8 @@ typedef enum csa2_kernel {
   CSA2_KERNEL_OPROJ_MFMA = 12,    /* oproj_mfma_kernel (bf16 grouped output projection, K split) */
   CSA2_KERNEL_OPROJ_GENERIC = 13, /* oproj_generic_kernel */
   CSA2_KERNEL_OPROJ_MFMA16 = 14,  /* oproj_mfma16_kernel (bf16 grouped output projection, <= 16 rows) */
-  CSA2_KERNEL_OPROJ_LDS = 15      /* oproj_lds_kernel (bf16 grouped output projection, 128 x 128 tiles) */
+  CSA2_KERNEL_OPROJ_LDS = 15,     /* oproj_lds_kernel (bf16 grouped output projection, 128 x 128 tiles) */
+  CSA2_KERNEL_READ_PROBE = 16     /* read_probe_kernel (csa2_read_probe) */
 } csa2_kernel;
 
 typedef struct csa2_trace_record {
@@ -348,6 +349,22 @@ int csa2_trace_read(csa2_trace_record* out, int32_t max, int32_t* n_dropped);
 
 /* Static name of a csa2_kernel: the name of its __global__ function. */
 const char* csa2_kernel_name(int32_t kernel);
+
+/* csa2_read_probe - measurement utility, not a step of the method.
+ *
+ * Reads `bytes` bytes of device buffer `buf` once with a plain coalesced
+ * streaming kernel (16-byte loads, 8 in flight per lane, 32 KB contiguous
+ * per workgroup and iteration).  Its device duration, taken from the kernel
+ * trace (CSA2_KERNEL_READ_PROBE), is the time this GPU needs to stream a
+ * working set of that size: the measured read ceiling that a bandwidth-bound
+ * kernel of the path is compared with, next to the published HBM peak.
+ *  buf    device pointer, 16-byte aligned, read only
+ *  bytes  a positive multiple of 16
+ *  sink   device uint32, written only if the XOR of every word read equals
+ *         a fixed constant (keeps the loads from being removed); may hold
+ *         anything before and after
+ * Enqueued on `stream`; allocates nothing.  Returns a csa2_status. */
+int csa2_read_probe(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

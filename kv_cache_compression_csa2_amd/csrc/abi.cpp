@@ -391,4 +391,19 @@ int csa2_grouped_out_proj(int32_t act_dtype, int32_t n_tok, int32_t width, int32
   }
 }
 
+int csa2_read_probe(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+  g_last_error.clear();
+  try {
+    if (bytes <= 0 || bytes % 16) return fail(CSA2_ERR_INVALID_ARG, "bytes=%lld: need a positive multiple of 16", (long long)bytes);
+    int st;
+    if ((st = check_ptr(buf, "buf"))) return st;
+    if (!sink) return fail(CSA2_ERR_INVALID_ARG, "sink is NULL");
+    clear_stale_error();
+    const hipError_t e = csa2::launch_read_probe(buf, bytes, sink, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? CSA2_OK : fail_hip(e, "read probe launch");
+  } catch (...) {
+    return fail(CSA2_ERR_HIP, "internal exception");
+  }
+}
+
 }  // extern "C"

@@ -98,6 +98,8 @@ hipError_t launch_kernel(int32_t kernel_id, K kern, dim3 grid, dim3 block, size_
 
 size_t attn_workspace_bytes(const csa2_dims& dims, const csa2_kv_cache& cache, int32_t n_q);
 
+hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream);
+
 hipError_t launch_oproj(int32_t act_dtype, int32_t n_tok, int32_t width, int32_t n_groups, int32_t rank,
                         const void* x, const void* w, void* y, hipStream_t stream);
 

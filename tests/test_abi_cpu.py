@@ -28,7 +28,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert B.csa2_abi_version() == 3
+    assert B.csa2_abi_version() == 4
     assert B.status_str(0) == "CSA2_OK"
     assert B.status_str(-4) == "CSA2_ERR_MODE_ORDER"
     assert B.status_str(-99) == "CSA2_ERR_UNKNOWN"
@@ -203,3 +203,13 @@ def test_grouped_out_proj_checks_pointers_and_allows_no_tokens():
     # no tokens: nothing to do, no pointer needed, no GPU call
     assert lib.csa2_grouped_out_proj(B.BF16, 0, 512, 8, 64, None, None, None, None) == 0
     assert B.last_error() == ""
+
+
+def test_read_probe_rejects_bad_arguments():
+    lib = B.library()
+    assert lib.csa2_read_probe(FAKE, 0, FAKE, None) == -1
+    assert lib.csa2_read_probe(FAKE, 24, FAKE, None) == -1
+    assert lib.csa2_read_probe(None, 1 << 20, FAKE, None) == -1
+    assert lib.csa2_read_probe(FAKE + 8, 1 << 20, FAKE, None) == -1
+    assert lib.csa2_read_probe(FAKE, 1 << 20, None, None) == -1
+    assert B.csa2_kernel_name(16) == "read_probe_kernel"
