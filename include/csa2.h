@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 4
+#define CSA2_ABI_VERSION 5
 
 typedef enum csa2_status {
   CSA2_OK = 0,
@@ -262,6 +262,29 @@ typedef struct csa2_compress_args {
 int csa2_layer_group(const csa2_dims* dims, const csa2_kv_cache* cache, int32_t n_layers,
                      const csa2_layer* layers, const int32_t* q_pos, int32_t n_q,
                      const csa2_compress_args* compress, void* ws, size_t ws_bytes, void* stream);
+
+/* csa2_layer_group_noalloc - csa2_layer_group for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.
+ *
+ * Same arguments (less the workspace), checks, kernels and results as
+ * csa2_layer_group.  The scratch the kernels need (indexer scores, block
+ * maxima, attention split partials: csa2_workspace_size(...,
+ * CSA2_EP_LAYER_GROUP, n_q) bytes) lives in a device array inside the
+ * library of CSA2_NOALLOC_SCRATCH_BYTES (64 MiB), one copy per GPU, held
+ * until the process ends.  That covers decode shapes (one query per
+ * sequence) of up to about 12 sequences at 1M entries or 16 at 256K; a call
+ * that needs more returns CSA2_ERR_WORKSPACE before any HIP work.  The first
+ * call on a device looks up that device's copy (hipGetSymbolAddress); no call
+ * allocates or frees memory.  Every call on one GPU uses the same array,
+ * which keeps the last call's contents (nothing in it has to start at zero):
+ * calls that overlap on one GPU - on different streams, or from different
+ * host threads - race, and the caller must order them.  Returns a
+ * csa2_status. */
+#define CSA2_NOALLOC_SCRATCH_BYTES (64u << 20)
+int csa2_layer_group_noalloc(const csa2_dims* dims, const csa2_kv_cache* cache, int32_t n_layers,
+                             const csa2_layer* layers, const int32_t* q_pos, int32_t n_q,
+                             const csa2_compress_args* compress, void* stream);
 
 /* csa2_grouped_out_proj - the grouped low-rank output projection after the
  * attention ([ZB] 1.2: o_lora_rank 1024 in o_groups 8).

@@ -90,6 +90,9 @@ _lib.csa2_sparse_attn.argtypes = [POINTER(Dims), POINTER(KVCache), c_void_p, c_v
 _lib.csa2_layer_group.restype = c_int
 _lib.csa2_layer_group.argtypes = [POINTER(Dims), POINTER(KVCache), c_int32, POINTER(Layer), c_void_p, c_int32,
                                   POINTER(CompressArgs), c_void_p, c_size_t, c_void_p]
+_lib.csa2_layer_group_noalloc.restype = c_int
+_lib.csa2_layer_group_noalloc.argtypes = [POINTER(Dims), POINTER(KVCache), c_int32, POINTER(Layer), c_void_p, c_int32,
+                                          POINTER(CompressArgs), c_void_p]
 _lib.csa2_grouped_out_proj.restype = c_int
 _lib.csa2_grouped_out_proj.argtypes = [c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                                        c_void_p]
@@ -104,7 +107,8 @@ _lib.csa2_kernel_name.argtypes = [c_int32]
 
 EXPORTED = ("csa2_compress", "csa2_index_topk", "csa2_sparse_attn", "csa2_layer_group", "csa2_workspace_size",
             "csa2_status_str", "csa2_last_error", "csa2_abi_version", "csa2_trace_enable", "csa2_trace_read",
-            "csa2_kernel_name", "csa2_grouped_out_proj", "csa2_read_probe")
+            "csa2_kernel_name", "csa2_grouped_out_proj", "csa2_read_probe",
+            "csa2_layer_group_noalloc")
 
 
 def library() -> ctypes.CDLL:
@@ -182,6 +186,13 @@ def csa2_layer_group(dims, cache, layers, q_pos, n_q, compress, ws, stream=None)
     _check(_lib.csa2_layer_group(ctypes.byref(dims), ctypes.byref(cache), len(layers), arr, ptr(q_pos), n_q,
                                  None if compress is None else ctypes.byref(compress), ptr(ws), ws_bytes,
                                  _stream(stream)))
+
+
+def csa2_layer_group_noalloc(dims, cache, layers, q_pos, n_q, compress, stream=None) -> None:
+    """csa2_layer_group with the library's own scratch (no workspace argument)."""
+    arr = (Layer * len(layers))(*layers)
+    _check(_lib.csa2_layer_group_noalloc(ctypes.byref(dims), ctypes.byref(cache), len(layers), arr, ptr(q_pos), n_q,
+                                         None if compress is None else ctypes.byref(compress), _stream(stream)))
 
 
 def csa2_grouped_out_proj(act_dtype, n_tok, width, n_groups, rank, x, w, y, stream=None) -> None:

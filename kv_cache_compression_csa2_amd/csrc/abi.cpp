@@ -138,6 +138,19 @@ int check_compress(const csa2_dims* d, const csa2_kv_cache* c, const void* laten
   return CSA2_OK;
 }
 
+int check_attn(const csa2_dims* dims, const void* q, const int32_t* q_pos, int32_t n_q, const int32_t* topk,
+                      const void* swa_kv, const int32_t* swa_first_pos, int32_t n_swa, void* out, const float* lse) {
+  int st;
+  if (n_q <= 0 || n_q > 65535) return fail(CSA2_ERR_INVALID_ARG, "n_q=%d out of range", n_q);
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(q_pos, "q_pos")) || (st = check_ptr(topk, "topk")) ||
+      (st = check_ptr(out, "out")))
+    return st;
+  if (n_swa < 0) return fail(CSA2_ERR_INVALID_ARG, "n_swa=%d is negative", n_swa);
+  if (n_swa > 0 && ((st = check_ptr(swa_kv, "swa_kv")) || (st = check_ptr(swa_first_pos, "swa_first_pos")))) return st;
+  if (lse && !aligned16(lse)) return fail(CSA2_ERR_INVALID_ARG, "lse is not 16-byte aligned");
+  return CSA2_OK;
+}
+
 // hipGetLastError() is per thread and sticky across unrelated runtime calls
 // (another library's probe may have left an error behind); clear it so that
 // the check after our launches reports only our launches.
@@ -163,6 +176,99 @@ int run_index(const csa2_dims* d, const csa2_kv_cache* c, const void* idx_q, con
 }
 
 }  // namespace
+
+namespace csa2 {
+
+int set_error(int status, const char* msg) { return fail(status, "%s", msg); }
+
+int layer_group_run(const csa2_dims* dims, const csa2_kv_cache* cache, int32_t n_layers, const csa2_layer* layers,
+                    const int32_t* q_pos, int32_t n_q, const csa2_compress_args* compress, const WorkspaceFn& get_ws,
+                    void* stream) {
+  int st;
+  if ((st = check_dims(dims))) return st;
+  if (n_layers <= 0 || n_layers > 64) return fail(CSA2_ERR_INVALID_ARG, "n_layers=%d: need 1..64", n_layers);
+  if (!layers) return fail(CSA2_ERR_INVALID_ARG, "layers is NULL");
+  bool need_idx = compress != nullptr;
+  for (int i = 0; i < n_layers; ++i) need_idx |= layers[i].mode != CSA2_REUSE;
+  if ((st = check_cache(dims, cache, need_idx))) return st;
+  if ((st = check_ptr(q_pos, "q_pos"))) return st;
+  if (compress) {
+    if (compress->reserved0 != 0) return fail(CSA2_ERR_INVALID_ARG, "compress reserved field must be 0");
+    if ((st = check_compress(dims, cache, compress->latent, compress->first_pos, compress->n_pos,
+                             compress->pair_logits, compress->w_ik)))
+      return st;
+  }
+  for (int i = 0; i < n_layers; ++i) {
+    const csa2_layer& L = layers[i];
+    if (L.mode == CSA2_FULL) {
+      if (L.source != -1) return fail(CSA2_ERR_MODE_ORDER, "layer %d: a Full layer has no source", i);
+      if (L.make_pool && !L.pool) return fail(CSA2_ERR_INVALID_ARG, "layer %d: make_pool needs a pool buffer", i);
+    } else if (L.mode == CSA2_REINDEX) {
+      if (L.source != -1) {
+        if (L.source < 0 || L.source >= i) return fail(CSA2_ERR_MODE_ORDER, "layer %d: Reindex source %d is not an earlier layer", i, L.source);
+        const csa2_layer& S = layers[L.source];
+        if (S.mode != CSA2_FULL || !S.make_pool)
+          return fail(CSA2_ERR_MODE_ORDER, "layer %d: Reindex source %d is not a Full layer with a pool", i, L.source);
+      }
+      if (L.make_pool) return fail(CSA2_ERR_INVALID_ARG, "layer %d: only Full layers build a pool", i);
+    } else if (L.mode == CSA2_REUSE) {
+      if (L.source < 0 || L.source >= i) return fail(CSA2_ERR_MODE_ORDER, "layer %d: Reuse source %d is not an earlier layer", i, L.source);
+      if (layers[L.source].mode == CSA2_REUSE)
+        return fail(CSA2_ERR_MODE_ORDER, "layer %d: Reuse source %d must be a Full or Reindex layer", i, L.source);
+      if (L.make_pool) return fail(CSA2_ERR_INVALID_ARG, "layer %d: only Full layers build a pool", i);
+    } else {
+      return fail(CSA2_ERR_UNSUPPORTED, "layer %d: mode %d unknown", i, L.mode);
+    }
+    if (L.mode != CSA2_REUSE) {
+      if ((st = check_ptr(L.idx_q, "layer idx_q")) || (st = check_ptr(L.head_w, "layer head_w")) ||
+          (st = check_ptr(L.topk, "layer topk")))
+        return st;
+    } else if (L.topk && !aligned16(L.topk)) {
+      return fail(CSA2_ERR_INVALID_ARG, "layer %d: topk is not 16-byte aligned", i);
+    }
+    if ((st = check_attn(dims, L.q, q_pos, n_q, L.mode == CSA2_REUSE ? layers[L.source].topk : L.topk, L.swa_kv,
+                         L.swa_first_pos, L.n_swa, L.out, L.lse)))
+      return st;
+  }
+  const size_t idx_bytes = round_up(index_ws_bytes(dims, cache, n_q), kAlign);
+  const size_t attn_bytes = attn_workspace_bytes(*dims, *cache, n_q);
+  void* ws = nullptr;
+  if ((st = get_ws(idx_bytes + attn_bytes, &ws))) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (compress &&
+      (st = run_compress(dims, cache, compress->latent, compress->first_pos, compress->n_pos, compress->pair_logits,
+                         compress->w_ik, s)))
+    return st;
+  void* attn_ws = static_cast<char*>(ws) + idx_bytes;
+  for (int i = 0; i < n_layers; ++i) {
+    const csa2_layer& L = layers[i];
+    const int32_t* use_topk = L.topk;
+    if (L.mode == CSA2_FULL) {
+      if ((st = run_index(dims, cache, L.idx_q, L.head_w, q_pos, n_q, nullptr, L.topk, L.make_pool ? L.pool : nullptr,
+                          nullptr, ws, s)))
+        return st;
+    } else if (L.mode == CSA2_REINDEX) {
+      const int32_t* pool_in = L.source >= 0 ? layers[L.source].pool : nullptr;
+      if ((st = run_index(dims, cache, L.idx_q, L.head_w, q_pos, n_q, pool_in, L.topk, nullptr, nullptr, ws, s)))
+        return st;
+    } else {
+      use_topk = layers[L.source].topk;
+      if (L.topk) {
+        hipError_t e = hipMemcpyAsync(L.topk, use_topk, sizeof(int32_t) * size_t(cache->batch) * n_q * dims->topk,
+                                      hipMemcpyDeviceToDevice, s);
+        if (e != hipSuccess) return fail_hip(e, "reuse top-k copy");
+      }
+    }
+    clear_stale_error();
+    hipError_t e = launch_attn(*dims, *cache, L.q, q_pos, n_q, use_topk, L.n_swa ? L.swa_kv : nullptr,
+                                     L.n_swa ? L.swa_first_pos : nullptr, L.n_swa, L.out, L.lse, attn_ws, attn_bytes, s);
+    if (e != hipSuccess) return fail_hip(e, "attention launch");
+  }
+  return CSA2_OK;
+}
+
+}  // namespace csa2
 
 extern "C" {
 
@@ -242,18 +348,6 @@ int csa2_index_topk(const csa2_dims* dims, const csa2_kv_cache* cache, const voi
   }
 }
 
-static int check_attn(const csa2_dims* dims, const void* q, const int32_t* q_pos, int32_t n_q, const int32_t* topk,
-                      const void* swa_kv, const int32_t* swa_first_pos, int32_t n_swa, void* out, const float* lse) {
-  int st;
-  if (n_q <= 0 || n_q > 65535) return fail(CSA2_ERR_INVALID_ARG, "n_q=%d out of range", n_q);
-  if ((st = check_ptr(q, "q")) || (st = check_ptr(q_pos, "q_pos")) || (st = check_ptr(topk, "topk")) ||
-      (st = check_ptr(out, "out")))
-    return st;
-  if (n_swa < 0) return fail(CSA2_ERR_INVALID_ARG, "n_swa=%d is negative", n_swa);
-  if (n_swa > 0 && ((st = check_ptr(swa_kv, "swa_kv")) || (st = check_ptr(swa_first_pos, "swa_first_pos")))) return st;
-  if (lse && !aligned16(lse)) return fail(CSA2_ERR_INVALID_ARG, "lse is not 16-byte aligned");
-  return CSA2_OK;
-}
 
 int csa2_sparse_attn(const csa2_dims* dims, const csa2_kv_cache* cache, const void* q, const int32_t* q_pos,
                      int32_t n_q, const int32_t* topk, const void* swa_kv, const int32_t* swa_first_pos,
@@ -279,91 +373,18 @@ int csa2_layer_group(const csa2_dims* dims, const csa2_kv_cache* cache, int32_t 
                      void* stream) {
   g_last_error.clear();
   try {
-    int st;
-    if ((st = check_dims(dims))) return st;
-    if (n_layers <= 0 || n_layers > 64) return fail(CSA2_ERR_INVALID_ARG, "n_layers=%d: need 1..64", n_layers);
-    if (!layers) return fail(CSA2_ERR_INVALID_ARG, "layers is NULL");
-    bool need_idx = compress != nullptr;
-    for (int i = 0; i < n_layers; ++i) need_idx |= layers[i].mode != CSA2_REUSE;
-    if ((st = check_cache(dims, cache, need_idx))) return st;
-    if ((st = check_ptr(q_pos, "q_pos"))) return st;
-    if (compress) {
-      if (compress->reserved0 != 0) return fail(CSA2_ERR_INVALID_ARG, "compress reserved field must be 0");
-      if ((st = check_compress(dims, cache, compress->latent, compress->first_pos, compress->n_pos,
-                               compress->pair_logits, compress->w_ik)))
-        return st;
-    }
-    for (int i = 0; i < n_layers; ++i) {
-      const csa2_layer& L = layers[i];
-      if (L.mode == CSA2_FULL) {
-        if (L.source != -1) return fail(CSA2_ERR_MODE_ORDER, "layer %d: a Full layer has no source", i);
-        if (L.make_pool && !L.pool) return fail(CSA2_ERR_INVALID_ARG, "layer %d: make_pool needs a pool buffer", i);
-      } else if (L.mode == CSA2_REINDEX) {
-        if (L.source != -1) {
-          if (L.source < 0 || L.source >= i) return fail(CSA2_ERR_MODE_ORDER, "layer %d: Reindex source %d is not an earlier layer", i, L.source);
-          const csa2_layer& S = layers[L.source];
-          if (S.mode != CSA2_FULL || !S.make_pool)
-            return fail(CSA2_ERR_MODE_ORDER, "layer %d: Reindex source %d is not a Full layer with a pool", i, L.source);
-        }
-        if (L.make_pool) return fail(CSA2_ERR_INVALID_ARG, "layer %d: only Full layers build a pool", i);
-      } else if (L.mode == CSA2_REUSE) {
-        if (L.source < 0 || L.source >= i) return fail(CSA2_ERR_MODE_ORDER, "layer %d: Reuse source %d is not an earlier layer", i, L.source);
-        if (layers[L.source].mode == CSA2_REUSE)
-          return fail(CSA2_ERR_MODE_ORDER, "layer %d: Reuse source %d must be a Full or Reindex layer", i, L.source);
-        if (L.make_pool) return fail(CSA2_ERR_INVALID_ARG, "layer %d: only Full layers build a pool", i);
-      } else {
-        return fail(CSA2_ERR_UNSUPPORTED, "layer %d: mode %d unknown", i, L.mode);
-      }
-      if (L.mode != CSA2_REUSE) {
-        if ((st = check_ptr(L.idx_q, "layer idx_q")) || (st = check_ptr(L.head_w, "layer head_w")) ||
-            (st = check_ptr(L.topk, "layer topk")))
-          return st;
-      } else if (L.topk && !aligned16(L.topk)) {
-        return fail(CSA2_ERR_INVALID_ARG, "layer %d: topk is not 16-byte aligned", i);
-      }
-      if ((st = check_attn(dims, L.q, q_pos, n_q, L.mode == CSA2_REUSE ? layers[L.source].topk : L.topk, L.swa_kv,
-                           L.swa_first_pos, L.n_swa, L.out, L.lse)))
-        return st;
-    }
-    const size_t idx_bytes = round_up(index_ws_bytes(dims, cache, n_q), kAlign);
-    const size_t attn_bytes = csa2::attn_workspace_bytes(*dims, *cache, n_q);
-    if ((st = check_ws(ws, ws_bytes, idx_bytes + attn_bytes))) return st;
-
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (compress &&
-        (st = run_compress(dims, cache, compress->latent, compress->first_pos, compress->n_pos, compress->pair_logits,
-                           compress->w_ik, s)))
-      return st;
-    void* attn_ws = static_cast<char*>(ws) + idx_bytes;
-    for (int i = 0; i < n_layers; ++i) {
-      const csa2_layer& L = layers[i];
-      const int32_t* use_topk = L.topk;
-      if (L.mode == CSA2_FULL) {
-        if ((st = run_index(dims, cache, L.idx_q, L.head_w, q_pos, n_q, nullptr, L.topk, L.make_pool ? L.pool : nullptr,
-                            nullptr, ws, s)))
-          return st;
-      } else if (L.mode == CSA2_REINDEX) {
-        const int32_t* pool_in = L.source >= 0 ? layers[L.source].pool : nullptr;
-        if ((st = run_index(dims, cache, L.idx_q, L.head_w, q_pos, n_q, pool_in, L.topk, nullptr, nullptr, ws, s)))
-          return st;
-      } else {
-        use_topk = layers[L.source].topk;
-        if (L.topk) {
-          hipError_t e = hipMemcpyAsync(L.topk, use_topk, sizeof(int32_t) * size_t(cache->batch) * n_q * dims->topk,
-                                        hipMemcpyDeviceToDevice, s);
-          if (e != hipSuccess) return fail_hip(e, "reuse top-k copy");
-        }
-      }
-      clear_stale_error();
-      hipError_t e = csa2::launch_attn(*dims, *cache, L.q, q_pos, n_q, use_topk, L.n_swa ? L.swa_kv : nullptr,
-                                       L.n_swa ? L.swa_first_pos : nullptr, L.n_swa, L.out, L.lse, attn_ws, attn_bytes, s);
-      if (e != hipSuccess) return fail_hip(e, "attention launch");
-    }
-    return CSA2_OK;
+    return csa2::layer_group_run(dims, cache, n_layers, layers, q_pos, n_q, compress,
+                                 [&](size_t need, void** out) -> int {
+                                   const int st = check_ws(ws, ws_bytes, need);
+                                   *out = ws;
+                                   return st;
+                                 },
+                                 stream);
   } catch (...) {
     return fail(CSA2_ERR_HIP, "internal exception");
   }
 }
+
 
 int csa2_grouped_out_proj(int32_t act_dtype, int32_t n_tok, int32_t width, int32_t n_groups, int32_t rank,
                           const void* x, const void* w, void* y, void* stream) {

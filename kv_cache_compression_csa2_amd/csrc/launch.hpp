@@ -9,6 +9,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <functional>
 
 #include "csa2.h"
 
@@ -97,6 +98,18 @@ hipError_t launch_kernel(int32_t kernel_id, K kern, dim3 grid, dim3 block, size_
 }
 
 size_t attn_workspace_bytes(const csa2_dims& dims, const csa2_kv_cache& cache, int32_t n_q);
+
+// csa2_layer_group's argument checks and launch sequence with the workspace
+// supplied by get_ws(need, &ws), called once after every argument check
+// passed and before the first launch; a nonzero status from it is returned
+// unchanged.  Errors are recorded as for the entry points; the caller clears
+// the last error and catches exceptions.
+using WorkspaceFn = std::function<int(size_t need, void** ws)>;
+int layer_group_run(const csa2_dims* dims, const csa2_kv_cache* cache, int32_t n_layers, const csa2_layer* layers,
+                    const int32_t* q_pos, int32_t n_q, const csa2_compress_args* compress, const WorkspaceFn& get_ws,
+                    void* stream);
+// Record `msg` as the last error of this thread and return `status`.
+int set_error(int status, const char* msg);
 
 hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream);
 

@@ -28,7 +28,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert B.csa2_abi_version() == 4
+    assert B.csa2_abi_version() == 5
     assert B.status_str(0) == "CSA2_OK"
     assert B.status_str(-4) == "CSA2_ERR_MODE_ORDER"
     assert B.status_str(-99) == "CSA2_ERR_UNKNOWN"
@@ -213,3 +213,21 @@ def test_read_probe_rejects_bad_arguments():
     assert lib.csa2_read_probe(FAKE + 8, 1 << 20, FAKE, None) == -1
     assert lib.csa2_read_probe(FAKE, 1 << 20, None, None) == -1
     assert B.csa2_kernel_name(16) == "read_probe_kernel"
+
+
+def test_noalloc_group_checks_arguments_and_its_scratch_limit_before_any_hip_call():
+    """csa2_layer_group_noalloc runs the same checks as csa2_layer_group and
+    refuses a shape whose scratch exceeds CSA2_NOALLOC_SCRATCH_BYTES (64 MiB)
+    with CSA2_ERR_WORKSPACE, before it touches the GPU."""
+    lib = B.library()
+    arr = (B.Layer * 1)(layer(B.REUSE, 0))
+    assert lib.csa2_layer_group_noalloc(ctypes.byref(dims()), ctypes.byref(cache()), 1, arr, FAKE, 1, None, None) == -4
+    arr = (B.Layer * 1)(layer(B.FULL))
+    big = cache(batch=64, capacity=1 << 20)  # 64 sequences x 1M entries: ~300 MB of scores
+    need = B.csa2_workspace_size(dims(), big, B.EP_LAYER_GROUP, 1)
+    assert need > 64 << 20
+    assert lib.csa2_layer_group_noalloc(ctypes.byref(dims()), ctypes.byref(big), 1, arr, FAKE, 1, None, None) == -3
+    assert "64 MiB" in B.last_error() or str(64 << 20) in B.last_error()
+    # the decode shapes it is for fit
+    for b, cap in ((16, 32768), (2, 1 << 20), (4, 1 << 18)):
+        assert B.csa2_workspace_size(dims(), cache(batch=b, capacity=cap), B.EP_LAYER_GROUP, 1) <= 64 << 20

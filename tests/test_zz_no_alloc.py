@@ -1,0 +1,53 @@
+"""csa2_layer_group_noalloc (the layer-group call with the library's own
+scratch, for callers that cannot allocate) against csa2_layer_group with a
+caller workspace: two calls in a row on one GPU, the second on a smaller
+shape than the first (so its scratch region still holds the first call's
+data), each bit-identical to the workspace entry point on the same inputs.
+"""
+import pytest
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _noalloc_matches_group(R, B, name):
+    import torch
+
+    wl = synth.get(name)
+    inp = synth.Inputs(wl)
+    print(f"[noalloc] {name}: batch {wl.batch}, context {wl.context}, layers {[p.mode for p in wl.layers]}", flush=True)
+    st = R.DeviceStep(wl, inp)
+    st.run()  # csa2_layer_group with the caller's workspace
+    torch.cuda.synchronize()
+    ref = [{k: (None if L[k] is None else L[k].clone()) for k in ("topk", "pool", "out", "lse")} for L in st.layers]
+    for L in st.layers:  # poison every output
+        L["topk"].fill_(-7)
+        L["out"].fill_(float("nan"))
+        L["lse"].fill_(float("nan"))
+        if L["pool"] is not None:
+            L["pool"].fill_(-7)
+    torch.cuda.synchronize()
+    # the same step through the allocation-free entry point (its compress
+    # rewrites the step's new entries with the same bytes)
+    B.csa2_layer_group_noalloc(st.dims, st.cache.struct(), st.layer_structs(), st.q_pos, wl.n_q, st.compress_args())
+    torch.cuda.synchronize()
+    for li, (want, L) in enumerate(zip(ref, st.layers)):
+        for k in ("topk", "pool", "out", "lse"):
+            if want[k] is not None:
+                assert torch.equal(want[k], L[k]), f"{name} layer {li}: {k} differs from csa2_layer_group"
+    need = B.csa2_workspace_size(st.dims, st.cache.struct(), B.EP_LAYER_GROUP, wl.n_q)
+    print(f"[noalloc] {name}: identical ({need} bytes of scratch)", flush=True)
+    return need
+
+
+def test_noalloc_group_matches_workspace_group_twice_shrinking():
+    import torch
+
+    assert torch.cuda.is_available()
+    from kv_cache_compression_csa2_amd import binding as B
+    from kv_cache_compression_csa2_amd import runner as R
+
+    first = _noalloc_matches_group(R, B, "group_small")  # Full(pool) + Reindex x2 + Reuse, 2 x 20001
+    second = _noalloc_matches_group(R, B, "hsi_small")  # Full(pool) + Reindex + Reuse, 2 x 9001
+    assert second < first
