@@ -329,7 +329,7 @@ __device__ __forceinline__ void select_body(int topk, int cand_blocks, int ratio
                                                      const float* __restrict__ scores, const float* __restrict__ bmax,
                                                      const float* __restrict__ sbmax, int64_t dom_cap,
                                                      int32_t* __restrict__ topk_out, int32_t* __restrict__ pool_out,
-                                                     float* __restrict__ topk_scores) {
+                                                     float* __restrict__ topk_scores, int split) {
   extern __shared__ uint32_t lds_raw[];
   lds_u32* lds = (lds_u32*)lds_raw;  // address-space cast into LDS
   constexpr int kGather = KCAND <= 4096 ? 4 : 8;  // loads in flight per thread in a gather
@@ -348,6 +348,11 @@ __device__ __forceinline__ void select_body(int topk, int cand_blocks, int ratio
 
   const int qi = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int64_t row = int64_t(b) * n_q + qi;
+  // split: two workgroups per row, blockIdx.z 0 builds the pool, 1 the flat top-k
+  if (split) {
+    if (blockIdx.z == 1) pool_out = nullptr;
+  }
+  const bool pool_only = split && blockIdx.z == 0;
   const int nsb = int(dom_cap / 64);
   const int nb = int(dom_cap / 8);
   const float* sc = scores + row * dom_cap;
@@ -387,6 +392,7 @@ __device__ __forceinline__ void select_body(int topk, int cand_blocks, int ratio
     // pool block ids (ascending), in place: thread x reads and writes lb[x] only
     for (int x = tid; x < npool; x += kNT) L.lb[x] = min(L.la[L.lb[x] >> 3] * 8 + (L.lb[x] & 7), uint32_t(nb - 1));
     for (int x = tid; x < cand_blocks; x += kNT) pool_out[row * cand_blocks + x] = x < npool ? int32_t(L.lb[x]) : -1;
+    if (pool_only) return;  // uniform: the other workgroup of the row selects the top-k
     __syncthreads();
     // The best topk blocks by their own maxima all lie in the pool when
     // topk <= cand_blocks - 1: the pool holds the best cand_blocks - 1 blocks
@@ -462,9 +468,9 @@ __device__ __forceinline__ void select_body(int topk, int cand_blocks, int ratio
       const int32_t *__restrict__ pool_in, const int32_t *__restrict__ n_entries,                             \
       const float *__restrict__ scores, const float *__restrict__ bmax, const float *__restrict__ sbmax,       \
       int64_t dom_cap, int32_t *__restrict__ topk_out, int32_t *__restrict__ pool_out,                        \
-      float *__restrict__ topk_scores
+      float *__restrict__ topk_scores, int split
 #define SELECT_PASS \
-  topk, cand_blocks, ratio, capacity, q_pos, n_q, pool_in, n_entries, scores, bmax, sbmax, dom_cap, topk_out, pool_out, topk_scores
+  topk, cand_blocks, ratio, capacity, q_pos, n_q, pool_in, n_entries, scores, bmax, sbmax, dom_cap, topk_out, pool_out, topk_scores, split
 
 __global__ __launch_bounds__(kNT) void select_kernel(SELECT_ARGS) { select_body<kMaxCand>(SELECT_PASS); }
 // two workgroups per compute unit: 32 waves, at most 64 registers each
@@ -496,10 +502,16 @@ hipError_t launch_select(const csa2_dims& dims, const csa2_kv_cache& cache, cons
   const int64_t most = std::max<int64_t>({nsb, 8 * std::min<int64_t>(nsb, m_max), 8 * int64_t(dims.topk)});
   const bool small = most <= kSmallCand;
   auto kern = small ? select_kernel_wide : select_kernel;
-  const hipError_t err = launch_kernel(CSA2_KERNEL_SELECT, kern, dim3(n_q, cache.batch), dim3(kNT),
+  // Few rows (decode) leave the GPU idle while a row's selection runs its
+  // long chain of dependent steps: the pool and the flat top-k then take a
+  // workgroup each and run side by side, instead of the top-k following the
+  // pool inside one workgroup.  Many rows (prefill) keep one workgroup per
+  // row, whose top-k reuses the pool's blocks (less work in total).
+  const int split = pool_out && int64_t(cache.batch) * n_q <= 128 ? 1 : 0;
+  const hipError_t err = launch_kernel(CSA2_KERNEL_SELECT, kern, dim3(n_q, cache.batch, split ? 2 : 1), dim3(kNT),
                                        select_lds(small ? kSmallCand : kMaxCand), stream, dims.topk,
                      dims.cand_blocks, cache.ratio, cache.capacity, q_pos, n_q, pool_in, cache.n_entries, ss.scores,
-                     ss.bmax, ss.sbmax, ss.dom_cap, topk_out, pool_out, topk_scores);
+                     ss.bmax, ss.sbmax, ss.dom_cap, topk_out, pool_out, topk_scores, split);
   return err;
 }
 

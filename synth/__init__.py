@@ -183,6 +183,13 @@ SMALL = {
                            rope_theta=160000.0, rope_factor=16.0, rope_orig_len=65536),
     "prefill_yarn": replace(WORKLOADS["prefill_128k"], name="prefill_yarn", prior=4096, new=512, n_q=512,
                             rope_theta=160000.0, rope_factor=16.0, rope_orig_len=65536),
+    # a top-1536 (from a pool of 2048, and flat): the selection's threshold
+    # level expands more than a thousand candidate blocks
+    "pool_wide": replace(
+        WORKLOADS["decode_32k"], name="pool_wide", batch=1, prior=20000, new=1, topk=1536,
+        layers=(LayerPlan("full", make_pool=True), LayerPlan("reindex", 0), LayerPlan("reuse", 1)),
+    ),
+    "topk_wide": replace(WORKLOADS["decode_32k"], name="topk_wide", batch=1, prior=16000, new=1, topk=1536),
     "decoder_prefill_small": replace(WORKLOADS["decoder_prefill_64k"], name="decoder_prefill_small", prior=8192,
                                      new=256, n_q=256, cand_blocks=64, topk=128),
     # FP8 (E4M3) window rows on every attention path: float32 generic, bf16
