@@ -95,8 +95,11 @@ int check_ptr(const void* p, const char* name) {
   return CSA2_OK;
 }
 
-int64_t dom_cap_flat(const csa2_kv_cache* c) { return int64_t(round_up(size_t(c->capacity), 256)); }
-int64_t dom_cap_pool(const csa2_dims* d) { return int64_t(round_up(size_t(d->cand_blocks) * 8, 256)); }
+// Domain slots per (sequence, query) in the scratch: whole workgroups of the
+// decode scan (16 super-blocks of 64 slots), so its stores need no bounds test.
+constexpr size_t kDomAlign = 1024;
+int64_t dom_cap_flat(const csa2_kv_cache* c) { return int64_t(round_up(size_t(c->capacity), kDomAlign)); }
+int64_t dom_cap_pool(const csa2_dims* d) { return int64_t(round_up(size_t(d->cand_blocks) * 8, kDomAlign)); }
 
 size_t index_ws_bytes(const csa2_dims* d, const csa2_kv_cache* c, int32_t n_q) {
   const int64_t cap = dom_cap_flat(c) > dom_cap_pool(d) ? dom_cap_flat(c) : dom_cap_pool(d);

@@ -151,8 +151,10 @@ __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__flo
 __device__ __forceinline__ int ord_int(int b) { return b ^ int(uint32_t(b >> 31) >> 1); }
 
 // Maximum with the value of another lane of the same 16-lane row, by DPP.
+// Every pattern used reads a lane inside the row, so bound_ctrl changes
+// nothing but lets the compiler fold the move into one v_max_i32_dpp.
 template <int CTRL>
-__device__ __forceinline__ int max_dpp(int k) { return max(k, __builtin_amdgcn_mov_dpp(k, CTRL, 0xF, 0xF, false)); }
+__device__ __forceinline__ int max_dpp(int k) { return max(k, __builtin_amdgcn_mov_dpp(k, CTRL, 0xF, 0xF, true)); }
 constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
 constexpr int kDppHalfMirror = 0x141; // lane i of each 8 <- lane 7 - i
@@ -189,13 +191,16 @@ __device__ __forceinline__ void scan_mfma_body(
     float* __restrict__ scores, float* __restrict__ bmax, float* __restrict__ sbmax, int64_t dom_cap) {
   constexpr int kTiles = 2 * kBatch;
   constexpr int kIters = kSbW / kBatch;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, h = lane >> 5;
   const int qi = blockIdx.y, b = blockIdx.z;
   const int64_t row = int64_t(b) * n_q + qi;
   const int nsb = int(dom_cap / 64);
   const int n_vis = int(visible_count(clamp_entries(n_entries, b, capacity), q_pos[row], ratio));
   const int sb0 = int(blockIdx.x) * (4 * kSbW) + wave;
+  const int last_tile = int(idx_rows_padded(capacity) / 32) - 1;
+  // this lane's bytes inside a tile: row n, and its half's first chunk
+  const uint32_t lane_off = uint32_t(n) * 16u + uint32_t(h) * (FP4 ? 512u : 4096u);
   // this sequence's rows (bf16: 256 bytes, FP4: 64 code bytes + 4 scale bytes)
   const uint8_t* kseq = idx_k + int64_t(b) * idx_rows_padded(capacity) * (FP4 ? 64 : 256);
   const uint8_t* sseq = FP4 ? idx_scale + int64_t(b) * capacity * 4 : nullptr;
@@ -204,17 +209,18 @@ __device__ __forceinline__ void scan_mfma_body(
   float* brow = bmax + row * (dom_cap / 8);
   float* sbrow = sbmax + row * nsb;
 
-  // The loads are issued unconditionally (slots past the domain read entry
-  // 0, masked later) and the loop holds no branch and no store, its stores
-  // deferred to the end: a load or a store under a branch makes the
-  // compiler's wait counts assume the branch was skipped, so each batch
-  // waited for the loads of the batch issued after it and the prefetch was
-  // void (FP4 1M scan 40.5 -> 35.5 us, 32K bf16 scan 26.7 -> 25.2 us).
+  // The loads and stores are issued unconditionally (slots past the visible
+  // entries read a valid row and are masked; every lane stores, the domain
+  // being whole workgroups of super-blocks): a load or a store under a
+  // branch makes the compiler's wait counts assume the branch was skipped,
+  // so each batch waited for the loads of the batch issued after it and the
+  // prefetch was void (FP4 1M scan 40.5 -> 35.5 us, 32K bf16 scan 26.7 ->
+  // 25.2 us).
   auto issue = [&](int it, ScanBatch<FP4, kBatch>& B) {
     const int sb_first = sb0 + 4 * kBatch * it;
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
-      const int sb = sb_first + 4 * (t >> 1);
+      const int sb = sb_first + 4 * (t >> 1);  // wave-uniform
       B.slot[t] = sb * 64 + 32 * (t & 1) + n;
       int j = B.slot[t];
       if constexpr (POOL) {
@@ -222,18 +228,30 @@ __device__ __forceinline__ void scan_mfma_body(
         j = blk >= 0 ? blk * 8 + (B.slot[t] & 7) : -1;
       }
       B.valid[t] = sb < nsb && j >= 0 && j < n_vis;
-      const int jj = B.valid[t] ? j : 0;
-      // tile jj / 32, row jj % 32: chunk c at (32 c + jj % 32) * 16
-      const uint8_t* tile = kseq + int64_t(jj >> 5) * (FP4 ? 2048 : 8192) + (jj & 31) * 16;
+      const uint8_t* tile;
+      int jj;  // the entry whose scales are read
+      if constexpr (POOL) {
+        jj = B.valid[t] ? j : 0;
+        // tile jj / 32, row jj % 32: chunk c at (32 c + jj % 32) * 16
+        tile = kseq + int64_t(jj >> 5) * (FP4 ? 2048 : 8192) + (jj & 31) * 16 + h * (FP4 ? 512 : 4096);
+      } else {
+        // slot = entry: the tile is the same for the whole wave (clamped to
+        // the sequence's last padded tile; rows past the visible ones are
+        // masked), so the address is a wave-uniform base plus the lane's
+        // fixed 32-bit offset and costs no per-lane arithmetic
+        const int tu = min(2 * sb + (t & 1), last_tile);
+        tile = kseq + int64_t(tu) * (FP4 ? 2048 : 8192) + lane_off;
+        jj = min(32 * tu + n, int(capacity) - 1);
+      }
       if constexpr (FP4) {
 #pragma unroll
-        for (int g2 = 0; g2 < 2; ++g2) B.kf[t][g2] = *reinterpret_cast<const uint4*>(tile + (2 * g2 + h) * 512);
+        for (int g2 = 0; g2 < 2; ++g2) B.kf[t][g2] = *reinterpret_cast<const uint4*>(tile + g2 * 1024);
         // the entry's four scale bytes as loaded: shifting them here would
         // wait for the load at issue time and void the prefetch
         B.ks[t] = *reinterpret_cast<const uint32_t*>(sseq + int64_t(jj) * 4);
       } else {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) B.kb[t][q] = *reinterpret_cast<const uint4*>(tile + (8 * h + q) * 512);
+        for (int q = 0; q < 8; ++q) B.kb[t][q] = *reinterpret_cast<const uint4*>(tile + q * 512);
       }
     }
     // keep the loads here, a batch ahead of their use (the scheduler would
@@ -249,34 +267,45 @@ __device__ __forceinline__ void scan_mfma_body(
 
   // A operand (indexer query) and the lane's 16 head weights, held for the whole scan
   const uint16_t* qrow = idx_q + (row * 32 + n) * 128;
-  uint4 qraw[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int k0 = FP4 ? 64 * (q >> 2) + 32 * h + 8 * (q & 3) : 64 * h + 8 * q;
-    qraw[q] = *reinterpret_cast<const uint4*>(qrow + k0);
-  }
   float wreg[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) wreg[r] = head_w[row * 32 + 8 * (r >> 2) + 4 * h + (r & 3)];
   bf16x8_t qop[FP4 ? 1 : 8];
-  f16x8_t qop16[FP4 ? 8 : 1];
+  // FP4: the fp16 operand stays in LDS ([chunk][lane]) and is read at each
+  // product: 32 registers fewer than holding it (30.5 against 31.9 us for
+  // the 1M FP4 scan)
+  const uint4* q_lds = nullptr;
   float unscale = 1.0f;
   if constexpr (FP4) {
-    uint32_t amax = 0;  // largest |q| of the query (bits of a non-negative float)
+    // The fp16 query (times 2^k) is the same for the workgroup's four waves:
+    // each converts two of the eight operand chunks of every lane, after one
+    // shared maximum fixes k, and all read the whole operand back from LDS.
+    __shared__ uint32_t q_amax[4];
+    __shared__ uint4 q_op[8][64];  // [chunk][lane]
+    uint4 qraw[2];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const uint32_t w4[4] = {qraw[q].x, qraw[q].y, qraw[q].z, qraw[q].w};
+    for (int c = 0; c < 2; ++c) {
+      const int q = 2 * wave + c;
+      qraw[c] = *reinterpret_cast<const uint4*>(qrow + 64 * (q >> 2) + 32 * h + 8 * (q & 3));
+    }
+    uint32_t amax = 0;  // largest |q| (bits of a non-negative float)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const uint32_t w4[4] = {qraw[c].x, qraw[c].y, qraw[c].z, qraw[c].w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) amax = max(amax, max((w4[i] << 16) & 0x7FFF0000u, w4[i] & 0x7FFF0000u));
     }
     amax = __ockl_wfred_max_u32(amax);
+    if (lane == 0) q_amax[wave] = amax;
+    __syncthreads();
+    amax = max(max(q_amax[0], q_amax[1]), max(q_amax[2], q_amax[3]));
     const int e = amax ? int(amax >> 23) - 127 : 0;  // floor(log2 max|q|)
     const int k = min(100, max(-100, 14 - e));
     const float up = __uint_as_float(uint32_t(127 + k) << 23);
     unscale = __uint_as_float(uint32_t(127 - k) << 23);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const uint32_t w4[4] = {qraw[q].x, qraw[q].y, qraw[q].z, qraw[q].w};
+    for (int c = 0; c < 2; ++c) {
+      const uint32_t w4[4] = {qraw[c].x, qraw[c].y, qraw[c].z, qraw[c].w};
       uint4 v;
       uint32_t* vv = reinterpret_cast<uint32_t*>(&v);
 #pragma unroll
@@ -284,15 +313,14 @@ __device__ __forceinline__ void scan_mfma_body(
         const f16x2_t pr = {_Float16(__uint_as_float(w4[i] << 16) * up), _Float16(__uint_as_float(w4[i] & 0xFFFF0000u) * up)};
         vv[i] = __builtin_bit_cast(uint32_t, pr);
       }
-      qop16[q] = __builtin_bit_cast(f16x8_t, v);
+      q_op[2 * wave + c][lane] = v;
     }
+    __syncthreads();
+    q_lds = &q_op[0][0];
   } else {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) qop[q] = as_bf16x8(qraw[q]);
+    for (int q = 0; q < 8; ++q) qop[q] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 64 * h + 8 * q));
   }
-
-  // per-lane results kept for the stores after the loop
-  float d_sc[kIters * kTiles], d_bm[kIters * kTiles], d_sbm[kIters * kBatch];
 
 #pragma unroll
   for (int it = 0; it < kIters; ++it) {
@@ -324,8 +352,8 @@ __device__ __forceinline__ void scan_mfma_body(
 #pragma unroll
             for (int t = 0; t < kTiles; ++t) {
               const uint32_t w4[4] = {B.kf[t][g2].x, B.kf[t][g2].y, B.kf[t][g2].z, B.kf[t][g2].w};
-              acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qop16[4 * g2 + sub], fp4x8_to_f16(w4[sub], sg[t][g2], mp[t][g2]),
-                                                              acc[t], 0, 0, 0);
+              acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, q_lds[(4 * g2 + sub) * 64 + lane]),
+                                                              fp4x8_to_f16(w4[sub], sg[t][g2], mp[t][g2]), acc[t], 0, 0, 0);
             }
           }
         }
@@ -351,39 +379,27 @@ __device__ __forceinline__ void scan_mfma_body(
         part += part1;
       }
       // the entry's score: the lane's 16 heads plus the other half's 16
+      // (both halves hold the same sum)
       float sc = add_halves(part) * unscale;
       if (!B.valid[t]) sc = -INFINITY;
-      d_sc[it * kTiles + t] = sc;
-      // block (8 lanes) and tile (32 lanes) maxima, as ordered integers
+      // block (8 lanes) and tile (32 lanes) maxima, as ordered integers; the
+      // butterflies leave each maximum in every lane it covers
       int m = ord_int(__float_as_int(sc));
       m = max_dpp<kDppXor1>(m);
       m = max_dpp<kDppXor2>(m);
       m = max_dpp<kDppHalfMirror>(m);
-      d_bm[it * kTiles + t] = __int_as_float(ord_int(m));
+      const float bmx = __int_as_float(ord_int(m));
       m = max_dpp<kDppMirror>(m);
       tmax[t] = max_row_pairs(m);
+      // every lane stores (lanes holding the same value write the same
+      // address), so no store sits under a branch: the domain is whole
+      // workgroups of super-blocks, every slot of this wave lies in it
+      const int slot = (sb0 + 4 * kBatch * it + 4 * (t >> 1)) * 64 + 32 * (t & 1) + n;
+      srow[slot] = sc;
+      brow[slot >> 3] = bmx;
     }
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      d_sbm[it * kBatch + u] = __int_as_float(ord_int(max(tmax[2 * u], tmax[2 * u + 1])));
-    }
-  }
-  {
-#pragma unroll
-    for (int it = 0; it < kIters; ++it) {
-#pragma unroll
-      for (int t = 0; t < kTiles; ++t) {
-        const int sb = sb0 + 4 * kBatch * it + 4 * (t >> 1);
-        const int slot = sb * 64 + 32 * (t & 1) + n;
-        if (sb < nsb && h == 0) srow[slot] = d_sc[it * kTiles + t];
-        if (sb < nsb && h == 0 && (n & 7) == 0) brow[slot / 8] = d_bm[it * kTiles + t];
-      }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int sb = sb0 + 4 * kBatch * it + 4 * u;
-        if (sb < nsb && lane == 0) sbrow[sb] = d_sbm[it * kBatch + u];
-      }
-    }
+    for (int u = 0; u < kBatch; ++u) sbrow[sb0 + 4 * kBatch * it + 4 * u] = __int_as_float(ord_int(max(tmax[2 * u], tmax[2 * u + 1])));
   }
 }
 

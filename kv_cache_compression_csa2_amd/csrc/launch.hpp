@@ -51,7 +51,7 @@ struct ScanScratch {
   float* scores;  // [batch*n_q][dom_cap]
   float* bmax;    // [batch*n_q][dom_cap/8]
   float* sbmax;   // [batch*n_q][dom_cap/64]
-  int64_t dom_cap;  // multiple of 64
+  int64_t dom_cap;  // multiple of 1024: the decode scan's workgroups cover it exactly
 };
 
 hipError_t launch_compress(const csa2_dims& dims, const csa2_kv_cache& cache, const void* latent,
