@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 5
+#define CSA2_ABI_VERSION 6
 
 typedef enum csa2_status {
   CSA2_OK = 0,
@@ -262,6 +262,43 @@ typedef struct csa2_compress_args {
 int csa2_layer_group(const csa2_dims* dims, const csa2_kv_cache* cache, int32_t n_layers,
                      const csa2_layer* layers, const int32_t* q_pos, int32_t n_q,
                      const csa2_compress_args* compress, void* ws, size_t ws_bytes, void* stream);
+
+/* csa2_layer_plan - the cross-layer plan of a CSA2 model (host logic, no GPU work).
+ *
+ * [ZB] 1.2 gives a model's schedule as per-layer compress ratios (0 = the
+ * layer keeps no compressed KV), the kv-source layers (which write a main KV
+ * and indexer K: 2, 8, 14, 20), the index-source layers (which compute their
+ * own top-k: 2, 8, 14, 20, 24, 28, 32, 36) and the candidate-source layer (the
+ * Full layer that builds the HSI pool: 20); [ZB] 2.3.3 describes the encoder
+ * blocks (a Full layer, then Reuse layers) and the decoder (a Full block, then
+ * Reindex blocks searching its pool), [ZB] 3.3.1 and 3.3.3 that reuse only
+ * flows from earlier to later layers.  Readings of those passages, applied per
+ * layer l (0-based):
+ *   ratio 0:              a window-only layer: group -1, mode -1, source -1
+ *   a kv-source layer:    opens the cache group l; mode CSA2_FULL (it must be
+ *                         an index source); make_pool = 1 if l is the
+ *                         candidate source
+ *   another index source: CSA2_REINDEX in the current group; source = the
+ *                         group's Full layer if that builds the pool, else -1
+ *                         (every visible entry)
+ *   any other layer:      CSA2_REUSE of the latest index-source layer of its
+ *                         group
+ * A layer with compressed KV belongs to the latest kv-source layer, which must
+ * have its ratio with no layer of another ratio in between.
+ *  ratios   host [n_layers]: 0, 1 or 2
+ *  kv_src   host [n_kv], idx_src host [n_idx]: ascending, distinct layer numbers
+ *  cand_src a kv-source layer, or -1 (no pool)
+ *  out      host [n_layers], written
+ * Returns CSA2_OK or CSA2_ERR_INVALID_ARG (csa2_last_error() says why). */
+typedef struct csa2_plan_layer {
+  int32_t group;     /* kv-source layer whose caches the layer uses; -1: window-only */
+  int32_t mode;      /* csa2_mode, or -1 for a window-only layer */
+  int32_t source;    /* REINDEX: the layer whose pool is searched, or -1; REUSE: the layer whose top-k
+                        is read; FULL: -1 (layer numbers, not positions in the group) */
+  int32_t make_pool; /* FULL: builds the HSI pool */
+} csa2_plan_layer;
+int csa2_layer_plan(int32_t n_layers, const int32_t* ratios, int32_t n_kv, const int32_t* kv_src, int32_t n_idx,
+                    const int32_t* idx_src, int32_t cand_src, csa2_plan_layer* out);
 
 /* csa2_layer_group_noalloc - csa2_layer_group for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops,

@@ -62,6 +62,10 @@ class TraceRecord(ctypes.Structure):
     _fields_ = [("kernel", c_int32), ("ms", ctypes.c_float)]
 
 
+class PlanLayer(ctypes.Structure):
+    _fields_ = [("group", c_int32), ("mode", c_int32), ("source", c_int32), ("make_pool", c_int32)]
+
+
 class CompressArgs(ctypes.Structure):
     _fields_ = [
         ("latent", c_void_p), ("first_pos", c_void_p), ("n_pos", c_int32), ("reserved0", c_int32),
@@ -90,6 +94,9 @@ _lib.csa2_sparse_attn.argtypes = [POINTER(Dims), POINTER(KVCache), c_void_p, c_v
 _lib.csa2_layer_group.restype = c_int
 _lib.csa2_layer_group.argtypes = [POINTER(Dims), POINTER(KVCache), c_int32, POINTER(Layer), c_void_p, c_int32,
                                   POINTER(CompressArgs), c_void_p, c_size_t, c_void_p]
+_lib.csa2_layer_plan.restype = c_int
+_lib.csa2_layer_plan.argtypes = [c_int32, POINTER(c_int32), c_int32, POINTER(c_int32), c_int32, POINTER(c_int32),
+                                 c_int32, POINTER(PlanLayer)]
 _lib.csa2_layer_group_noalloc.restype = c_int
 _lib.csa2_layer_group_noalloc.argtypes = [POINTER(Dims), POINTER(KVCache), c_int32, POINTER(Layer), c_void_p, c_int32,
                                           POINTER(CompressArgs), c_void_p]
@@ -108,7 +115,7 @@ _lib.csa2_kernel_name.argtypes = [c_int32]
 EXPORTED = ("csa2_compress", "csa2_index_topk", "csa2_sparse_attn", "csa2_layer_group", "csa2_workspace_size",
             "csa2_status_str", "csa2_last_error", "csa2_abi_version", "csa2_trace_enable", "csa2_trace_read",
             "csa2_kernel_name", "csa2_grouped_out_proj", "csa2_read_probe",
-            "csa2_layer_group_noalloc")
+            "csa2_layer_group_noalloc", "csa2_layer_plan")
 
 
 def library() -> ctypes.CDLL:
@@ -186,6 +193,15 @@ def csa2_layer_group(dims, cache, layers, q_pos, n_q, compress, ws, stream=None)
     _check(_lib.csa2_layer_group(ctypes.byref(dims), ctypes.byref(cache), len(layers), arr, ptr(q_pos), n_q,
                                  None if compress is None else ctypes.byref(compress), ptr(ws), ws_bytes,
                                  _stream(stream)))
+
+
+def csa2_layer_plan(ratios, kv_src, idx_src, cand_src) -> list[tuple[int, int, int, int]]:
+    """(group, mode, source, make_pool) per layer, from host lists (see csa2.h)."""
+    n = len(ratios)
+    arr = lambda xs: (c_int32 * max(1, len(xs)))(*xs)
+    out = (PlanLayer * n)()
+    _check(_lib.csa2_layer_plan(n, arr(ratios), len(kv_src), arr(kv_src), len(idx_src), arr(idx_src), cand_src, out))
+    return [(p.group, p.mode, p.source, p.make_pool) for p in out]
 
 
 def csa2_layer_group_noalloc(dims, cache, layers, q_pos, n_q, compress, stream=None) -> None:

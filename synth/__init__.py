@@ -58,6 +58,7 @@ class Workload:
     rope_factor: float = 1.0  # YaRN factor (1 = plain RoPE)
     rope_orig_len: int = 0  # YaRN original context length
     swa: str = "act"  # window-row storage: "act" (the activation dtype) or "fp8" (E4M3 bytes)
+    swa_replay: bool = False  # window buffer limited to the queries' own segment (bounded replay)
     description: str = ""
 
     @property
@@ -77,9 +78,11 @@ class Workload:
         return np.broadcast_to(t, (self.batch, self.n_q)).copy()
 
     def swa_span(self) -> tuple[int, int]:
-        """First window position needed and number of window rows per sequence."""
+        """First window position held in the window buffer and its number of rows
+        per sequence: every row the queries' windows reach, or with bounded
+        replay only the queries' own segment."""
         t0 = self.context - self.n_q
-        first = max(0, t0 - self.window + 1)
+        first = t0 if self.swa_replay else max(0, t0 - self.window + 1)
         return first, self.context - first
 
 
@@ -156,6 +159,25 @@ WORKLOADS["decoder_prefill_64k"] = replace(
     "Full with per-query HSI pools + 2 Reindex layers",
 )
 
+# The decoder's cache group in the pages' schedule (zartbot walkthrough 1.2 and
+# 2.3.3; csa2_layer_plan derives it): layer 20 Full with the HSI pool, three
+# Reuse layers, then four blocks of a Reindex layer over the pool and three
+# Reuse layers of it (positions inside the group).
+DECODER_GROUP = (LayerPlan("full", make_pool=True),) + (LayerPlan("reuse", 0),) * 3 + sum(
+    ((LayerPlan("reindex", 0),) + (LayerPlan("reuse", 4 * i),) * 3 for i in range(1, 5)), ())
+
+# Decoder SWA bounded replay (zartbot walkthrough 2.2.2; 36Kr "FP4 and
+# Bounded Replay"): after an early-exit prefill only the last n_win = 128
+# prompt positions run through the decoder, each attending to its kept
+# entries and to window rows inside the replayed segment only.  The 64K
+# prompt's decoder group, for the 128 replayed queries.
+WORKLOADS["replay_64k"] = replace(
+    WORKLOADS["decode_32k"], name="replay_64k", batch=1, prior=65536 - 128, new=128, n_q=128,
+    layers=DECODER_GROUP, swa_replay=True,
+    description="decoder SWA bounded replay, bf16: the last 128 positions of a 65536-token prompt through the "
+    "decoder group (Full with per-query pools, 4 Reindex, 15 Reuse), windows cut to the replayed segment",
+)
+
 # Smaller cases of the same shapes, for parity at sizes the oracle finishes in seconds.
 SMALL = {
     "tiny_bf16": replace(WORKLOADS["tiny_encoder"], name="tiny_bf16", act="bf16", kv="bf16"),
@@ -190,6 +212,10 @@ SMALL = {
         layers=(LayerPlan("full", make_pool=True), LayerPlan("reindex", 0), LayerPlan("reuse", 1)),
     ),
     "topk_wide": replace(WORKLOADS["decode_32k"], name="topk_wide", batch=1, prior=16000, new=1, topk=1536),
+    # bounded replay: 128 queries whose windows stop at the segment start, the decoder group's modes
+    "replay_small": replace(WORKLOADS["replay_64k"], name="replay_small", prior=6000 - 128, cand_blocks=64,
+                            topk=128, layers=(LayerPlan("full", make_pool=True), LayerPlan("reuse", 0),
+                                              LayerPlan("reindex", 0), LayerPlan("reuse", 2))),
     "decoder_prefill_small": replace(WORKLOADS["decoder_prefill_64k"], name="decoder_prefill_small", prior=8192,
                                      new=256, n_q=256, cand_blocks=64, topk=128),
     # FP8 (E4M3) window rows on every attention path: float32 generic, bf16

@@ -28,7 +28,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert B.csa2_abi_version() == 5
+    assert B.csa2_abi_version() == 6
     assert B.status_str(0) == "CSA2_OK"
     assert B.status_str(-4) == "CSA2_ERR_MODE_ORDER"
     assert B.status_str(-99) == "CSA2_ERR_UNKNOWN"

@@ -22,11 +22,12 @@ FULL = {
     "decode_32k": ([0, 15], None),
     "group_256k": ([3], None),
     "fp4_1m": ([1], None),
-    "prefill_128k": ([0], [0, 1, 777, 2048, 4095]),
-    "encoder_block_128k": ([0], [0, 2047, 4095]),
+    "prefill_128k": ([0], [0, 1, 2, 255, 256, 511, 777, 1024, 1500, 2047, 2048, 2049, 3000, 3583, 4094, 4095]),
+    "encoder_block_128k": ([0], [0, 1, 1023, 2047, 2048, 3071, 4094, 4095]),
     "fp4_1m_pages": ([0], None),
     "decoder_prefill_64k": ([0], [0, 2049, 4095]),
     "fp4_1m_yarn": ([1], None),
+    "replay_64k": ([0], [0, 1, 64, 126, 127]),
 }
 
 
