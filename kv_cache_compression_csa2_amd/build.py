@@ -59,5 +59,46 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+# Host files built with AddressSanitizer and UndefinedBehaviorSanitizer for
+# the CPU check (each -fsanitize applies to the host code only; device code
+# is built as usual)
+HOST_SOURCES = ("abi.cpp", "plan.cpp", "trace.cpp", "noalloc.hip")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def build_host_check() -> str:
+    """Build csrc_check/abi_host_check.cpp against the library's host files
+    built with the sanitizers (the other sources' objects from build());
+    returns the executable's path."""
+    san = os.path.join(BUILD, "san")
+    os.makedirs(san, exist_ok=True)
+    objs = []
+    for f in HOST_SOURCES:
+        obj = os.path.join(san, f + ".o")
+        cmd = [HIPCC, *CFLAGS, *SAN_FLAGS, "-c", os.path.join(CSRC, f), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        objs.append(obj)
+    others = [os.path.join(BUILD, os.path.basename(src) + ".o") for src in sources()
+              if os.path.basename(src) not in HOST_SOURCES]
+    missing = [o for o in others if not os.path.exists(o)]
+    if missing:
+        build(verbose=False)
+    driver = os.path.join(ROOT, "kv_cache_compression_csa2_amd", "csrc_check", "abi_host_check.cpp")
+    drv_obj = os.path.join(san, "abi_host_check.o")
+    cmd = [HIPCC, *CFLAGS, *SAN_FLAGS, "-c", driver, "-o", drv_obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    exe = os.path.join(san, "abi_host_check")
+    cmd = [HIPCC, f"--offload-arch={ARCH}", *SAN_FLAGS, drv_obj, *objs, *others, "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return exe
+
+
 if __name__ == "__main__":
     build()
