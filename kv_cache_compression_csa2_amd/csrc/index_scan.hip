@@ -457,8 +457,8 @@ constexpr int kQB = 1;                // query blocks per workgroup, in turn, sh
 constexpr int kEB = 2;                // 32-entry blocks per wave (its resident K: 32 kEB registers)
 constexpr int kPE = 4 * 32 * kEB;     // entries per workgroup
 constexpr int kQTile = kPQ * 256;     // one head's query rows (bytes)
-constexpr int kHPS = 2;               // heads per LDS stage (even): one workgroup barrier per stage
-constexpr int kStages = 3;            // stages in LDS: kStages - 1 stages' copies fly
+constexpr int kHPS = 4;               // heads per LDS stage (even): one workgroup barrier per stage
+constexpr int kStages = 2;            // stages in LDS: kStages - 1 stages' copies fly
 constexpr int kNStage = 32 / kHPS;    // stages per query block
 
 typedef float f32x16_t_ __attribute__((__vector_size__(64)));
@@ -561,31 +561,49 @@ __global__ __launch_bounds__(256, 2) void scan_prefill_kernel(
     for (int blk = 0; blk < kEB; ++blk) sacc[blk] = f32x16_t_{};
 
     if (e_wg < vmax) {
-      // logits of head hh from tile `qt` into acc
-      auto contract = [&](const uint8_t* qt, f32x16_t_* acc) {
-#pragma unroll
-        for (int blk = 0; blk < kEB; ++blk) acc[blk] = f32x16_t_{};
+      // Software pipeline over the heads: each k-step's query operand of
+      // head h+1 is read from LDS into the register of head h's operand as
+      // soon as head h's two products have taken it (eight operands live, a
+      // head of products to arrive), and head h-1's ReLU.w fold is
+      // interleaved with head h's products (a product, then four VALU
+      // instructions), so one wave keeps the matrix pipe fed while its VALU
+      // and LDS work proceed.  Head h-1's logits are complete by then (its
+      // last product issued one product earlier).  The stage barrier sits
+      // before a stage's last head, during which the next stage's first
+      // head is read.
+      // head products into acc, reading the next head's operands from tile
+      // `nqt` into op, interleaved with fold(w_prev, prev): scores +=
+      // w_prev * max(0, logit) (ReLU as an integer max on the bits)
+      auto head_step = [&](bf16x8_t (&op)[8], f32x16_t_* acc, const uint8_t* nqt, float w_prev,
+                           const f32x16_t_* prev) {
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(qt + 16 * qslot(n, 2 * s + hl));
 #pragma unroll
           for (int blk = 0; blk < kEB; ++blk)
-            acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[blk][s]), a, acc[blk], 0, 0, 0);
+            acc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kreg[blk][s]), op[s],
+                                                               s == 0 ? f32x16_t_{} : acc[blk], 0, 0, 0);
+          op[s] = *reinterpret_cast<const bf16x8_t*>(nqt + 16 * qslot(n, 2 * s + hl));
         }
-      };
-      // scores += w_hh * max(0, logit); max(0, x) as an integer max on the bits
-      auto fold = [&](int hh, const f32x16_t_* acc) {
-        const float w = wl[hh][n];
 #pragma unroll
         for (int blk = 0; blk < kEB; ++blk)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            sacc[blk][r] += w * __int_as_float(max(__float_as_int(acc[blk][r]), 0));
+            sacc[blk][r] += w_prev * __int_as_float(max(__float_as_int(prev[blk][r]), 0));
+        // per k-step: a product, four VALU, the other product, the operand read, four VALU
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
       };
-      f32x16_t_ acc_a[kEB], acc_b[kEB];
-      for (int p = 0; p < kNStage; ++p) {
-        // this wave's copies of stage p landed; those of the stages after it
-        // (at most kStages - 2, 2 kHPS instructions each) may still fly
+      // this wave's copies of stage p landed (those of the stages after it,
+      // at most kStages - 2 of 2 kHPS instructions each, may still fly);
+      // after the barrier every wave's copies are visible and the slot of
+      // stage p - 1 is free for stage p + kStages - 1
+      auto stage_ready = [&](int p) {
         const int ahead = min(kStages - 2, kNStage - 1 - p) * 2 * kHPS;
         if (ahead >= 16)
           asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
@@ -595,20 +613,47 @@ __global__ __launch_bounds__(256, 2) void scan_prefill_kernel(
           asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
         else
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();  // every wave's copies of stage p landed; stage p-1's slot is free
+        __syncthreads();
         if (p + kStages - 1 < kNStage) issue_pair(p + kStages - 1, q0);
-        if (!wave_live) continue;
+      };
+      bf16x8_t op[8];
+      f32x16_t_ acc0[kEB], acc1[kEB];
+#pragma unroll
+      for (int blk = 0; blk < kEB; ++blk) acc1[blk] = f32x16_t_{};  // "head -1": folds nothing
+      stage_ready(0);
+      if (wave_live) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) op[s] = *reinterpret_cast<const bf16x8_t*>(qtile[0] + 16 * qslot(n, 2 * s + hl));
+      }
+      for (int p = 0; p < kNStage; ++p) {  // heads kHPS p + j: even j into acc0, odd into acc1
         const uint8_t* qt = qtile[kHPS * (p % kStages)];
 #pragma unroll
-        for (int j = 0; j < kHPS; j += 2) {
+        for (int j = 0; j < kHPS; ++j) {
           const int h = kHPS * p + j;
-          contract(qt + j * kQTile, acc_a);               // head h
-          if (h > 0) fold(h - 1, acc_b);                  // head h-1, under head h's products
-          contract(qt + (j + 1) * kQTile, acc_b);         // head h+1
-          fold(h, acc_a);                                 // head h, under head h+1's products
+          const uint8_t* nqt;  // the tile of head h + 1
+          if (j + 1 < kHPS) {
+            nqt = qt + (j + 1) * kQTile;
+          } else {
+            if (p + 1 < kNStage) stage_ready(p + 1);
+            // after the last stage the reads re-read this stage (never used)
+            nqt = qtile[kHPS * ((p + 1 < kNStage ? p + 1 : p) % kStages)];
+          }
+          if (wave_live) {
+            const float w_prev = h > 0 ? wl[h - 1][n] : 0.0f;
+            if (j % 2 == 0)
+              head_step(op, acc0, nqt, w_prev, acc1);
+            else
+              head_step(op, acc1, nqt, w_prev, acc0);
+          }
         }
       }
-      if (wave_live) fold(31, acc_b);
+      if (wave_live) {
+        const float w = wl[31][n];
+#pragma unroll
+        for (int blk = 0; blk < kEB; ++blk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[blk][r] += w * __int_as_float(max(__float_as_int(acc1[blk][r]), 0));
+      }
     }
 
     // ---- mask, store scores and maxima ----
