@@ -241,11 +241,12 @@ struct TileMask {
 };
 
 // FP4: the cache is FP4 with one E4M3 scale per MG channels (MG = 16 or 32).
-// SHARE (64 heads, many queries): one workgroup per query, wave w owns heads
-// 16w .. 16w+15, and the four waves run every row tile together from a
-// shared ring of two slabs, each wave copying (and for FP4 dequantising) four
-// of the tile's 16 rows: a row is gathered once per query instead of once per
-// head group.  No row splits, no cross-wave combine.
+// SHARE (64 heads, many queries): one workgroup per (query, row split), wave
+// w owns heads 16w .. 16w+15, and the four waves run every row tile together
+// from a shared ring of two slabs, each wave copying (and for FP4
+// dequantising) four of the tile's 16 rows: a row is gathered once per query
+// instead of once per head group.  No cross-wave combine; with row splits
+// each wave stores its heads' unnormalised output for attn_merge_kernel.
 // W8: window rows are E4M3 (FN) bytes, copied as they are and widened to
 // bf16 in the slab (exact) before the tile is used.
 template <bool FP4, int MG, bool SHARE, bool W8>
@@ -263,11 +264,14 @@ __global__ __launch_bounds__(256, SHARE && !FP4 ? 2 : 1) void attn_mfma_kernel(
   int hg, split;
   int64_t bq;
   if constexpr (SHARE) {
-    // workgroup -> query: consecutive queries (which share window rows) on one XCD
+    // workgroup -> (query, row split): consecutive queries (which share
+    // window rows) on one XCD
     hg = wave;
-    split = 0;
-    bq = x8 * ((n_bq + 7) / 8) + rest;
-    if (bq >= n_bq) return;  // padding workgroup (uniform)
+    const int64_t n_pairs = n_bq * n_splits;
+    const int64_t pair = x8 * ((n_pairs + 7) / 8) + rest;
+    if (pair >= n_pairs) return;  // padding workgroup (uniform)
+    bq = pair / n_splits;
+    split = int(pair % n_splits);
   } else {
     // workgroup -> (query, split, head group): the G head groups of one
     // (query, split) pair share an XCD (id % 8), the pairs go round the XCDs
@@ -542,11 +546,22 @@ __global__ __launch_bounds__(256, SHARE && !FP4 ? 2 : 1) void attn_mfma_kernel(
       compute(1, mb, false);
       ++tile;
     }
-    // each wave owns its heads: normalise and store, no combine
+    // each wave owns its heads: no combine; normalise and store, or with
+    // row splits store the unnormalised output and (reference max, sum)
     l_part += __shfl_xor(l_part, 16, kWave);
     l_part += __shfl_xor(l_part, 32, kWave);
-    const float inv = l_part > 0.0f ? 1.0f / l_part : 0.0f;
     const int64_t head = int64_t(wave) * 16 + l16;
+    if (n_splits > 1) {
+      const int64_t prow = (bq * n_splits + split) * H + head;
+#pragma unroll
+      for (int cb = 0; cb < 32; ++cb) *reinterpret_cast<f32x4*>(part_o + prow * kD + 16 * cb + 4 * g) = oacc[cb];
+      if (g == 0) {
+        part_ml[prow * 2] = m_ref;
+        part_ml[prow * 2 + 1] = l_part;
+      }
+      return;
+    }
+    const float inv = l_part > 0.0f ? 1.0f / l_part : 0.0f;
 #pragma unroll
     for (int cb = 0; cb < 32; ++cb) {
       uint2 pk;
@@ -679,10 +694,14 @@ struct AttnPlan {
   int64_t n_blocks;  // 1-D grid of the MFMA kernel
 };
 
-// Row splits per (query, head group): one while the (query, head group)
-// workgroups alone fill the 256 compute units, otherwise enough to reach
-// about 256 workgroups (each wave's tile stream is latency-bound, so more
-// workgroups in flight beat the cost of merging the splits).
+// Queries of 64 heads from kShareMinQueries up take one workgroup per query
+// whose waves share each row tile (SHARE), with row splits while the queries
+// alone do not fill the compute units; fewer queries (decode) take a
+// workgroup per (query, head group), with row splits up to about 256
+// workgroups.  Each wave's tile
+// stream is latency-bound, so more workgroups in flight beat the cost of
+// merging the splits.
+constexpr int64_t kShareMinQueries = 128;  // 64 queries: per head group 24.6 us, shared 28.7 us
 AttnPlan plan_attn(const csa2_dims& dims, const csa2_kv_cache& cache, int32_t n_q) {
   AttnPlan p{};
   p.mfma = dims.d == kD && dims.n_heads % 16 == 0 && dims.act_dtype == CSA2_BF16 &&
@@ -692,17 +711,25 @@ AttnPlan plan_attn(const csa2_dims& dims, const csa2_kv_cache& cache, int32_t n_
   p.n_splits = 1;
   if (!p.mfma || n_q <= 0) return p;
   const int64_t n_bq = int64_t(cache.batch) * n_q, G = dims.n_heads / 16;
-  if (dims.n_heads == 64 && n_bq >= 256) {  // enough queries to fill the chip one per workgroup
+  auto set_splits = [&](int64_t units, int64_t target) {
+    int splits = int(units >= target ? 1 : (target + units - 1) / units);
+    splits = splits < 1 ? 1 : (splits > p.n_tiles ? p.n_tiles : splits);
+    splits = splits > kMaxSplits ? kMaxSplits : splits;
+    p.tiles_per_split = (p.n_tiles + splits - 1) / splits;
+    p.n_splits = (p.n_tiles + p.tiles_per_split - 1) / p.tiles_per_split;
+  };
+  if (dims.n_heads == 64 && n_bq >= kShareMinQueries) {
+    // one workgroup per (query, row split): bf16 rows split up to about 256
+    // workgroups (a 128-query replay segment: 2 splits, 47 -> 41 us per
+    // layer with the merge; 4 splits 46 us, their partials cost more than
+    // the parallelism gains); FP4 rows never split (a 200-query chunk: 103
+    // us unsplit, 120-123 us + merge split, 142 us per head group)
     p.share = true;
-    p.n_blocks = 8 * ((n_bq + 7) / 8);
+    set_splits(n_bq, cache.kv_dtype == CSA2_FP4 ? 128 : 256);
+    p.n_blocks = 8 * ((n_bq * p.n_splits + 7) / 8);
     return p;
   }
-  const int64_t units = n_bq * G;
-  int splits = int(units >= 256 ? 1 : (256 + units - 1) / units);
-  splits = splits < 1 ? 1 : (splits > p.n_tiles ? p.n_tiles : splits);
-  splits = splits > kMaxSplits ? kMaxSplits : splits;
-  p.tiles_per_split = (p.n_tiles + splits - 1) / splits;
-  p.n_splits = (p.n_tiles + p.tiles_per_split - 1) / p.tiles_per_split;
+  set_splits(n_bq * G, 256);
   p.n_blocks = 8 * G * ((n_bq * p.n_splits + 7) / 8);
   return p;
 }

@@ -227,6 +227,13 @@ SMALL = {
                               swa="fp8"),
     "prefill_fp4_fp8win": replace(WORKLOADS["prefill_128k"], name="prefill_fp4_fp8win", kv="fp4", prior=4096,
                                   new=512, n_q=512, swa="fp8"),
+    # small chunks: 64 queries (a workgroup per head group), 128-255 queries
+    # (a workgroup per query; bf16 rows with row splits, FP4 rows without)
+    "chunk_small": replace(WORKLOADS["prefill_128k"], name="chunk_small", prior=4096, new=64, n_q=64),
+    "chunk_fp4_small": replace(WORKLOADS["prefill_128k"], name="chunk_fp4_small", kv="fp4", prior=4096, new=200,
+                               n_q=200),
+    "chunk_fp8win": replace(WORKLOADS["prefill_128k"], name="chunk_fp8win", prior=4096, new=160, n_q=160,
+                            swa="fp8"),
 }
 
 ALL = {**WORKLOADS, **SMALL}
