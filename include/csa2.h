@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 6
+#define CSA2_ABI_VERSION 7
 
 typedef enum csa2_status {
   CSA2_OK = 0,
@@ -385,7 +385,8 @@ typedef enum csa2_kernel {
   CSA2_KERNEL_OPROJ_GENERIC = 13, /* oproj_generic_kernel */
   CSA2_KERNEL_OPROJ_MFMA16 = 14,  /* oproj_mfma16_kernel (bf16 grouped output projection, <= 16 rows) */
   CSA2_KERNEL_OPROJ_LDS = 15,     /* oproj_lds_kernel (bf16 grouped output projection, 128 x 128 tiles) */
-  CSA2_KERNEL_READ_PROBE = 16     /* read_probe_kernel (csa2_read_probe) */
+  CSA2_KERNEL_READ_PROBE = 16,    /* read_probe_kernel (csa2_read_probe) */
+  CSA2_KERNEL_MFMA_PROBE = 17     /* mfma_probe_kernel (csa2_mfma_probe) */
 } csa2_kernel;
 
 typedef struct csa2_trace_record {
@@ -425,6 +426,26 @@ const char* csa2_kernel_name(int32_t kernel);
  *         anything before and after
  * Enqueued on `stream`; allocates nothing.  Returns a csa2_status. */
 int csa2_read_probe(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
+
+/* csa2_mfma_probe - measurement utility, not a step of the method.
+ *
+ * Runs `workgroups` workgroups of 4 waves, two per compute unit, each wave
+ * doing CSA2_MFMA_PROBE_CHAINS independent chains of `iters` bf16 matrix
+ * products of 32 x 32 x 16 (v_mfma_f32_32x32x16_bf16, fp32 accumulation) on
+ * register operands, with no memory traffic but one conditional store:
+ * workgroups * CSA2_MFMA_PROBE_FLOP_PER_WG_ITER * iters flops.  Its device
+ * duration, taken from the kernel trace (CSA2_KERNEL_MFMA_PROBE), gives the
+ * bf16 matrix-core rate this GPU sustains under a full matrix load (at the
+ * clock it holds then): the measured ceiling that the matrix-bound indexer
+ * scan is compared with, next to the published peak.
+ *  iters       1 .. 2^24
+ *  workgroups  1 .. 65536
+ *  sink        device float, written only if the accumulated sum equals a
+ *              fixed constant (keeps the products from being removed)
+ * Enqueued on `stream`; allocates nothing.  Returns a csa2_status. */
+#define CSA2_MFMA_PROBE_CHAINS 8
+#define CSA2_MFMA_PROBE_FLOP_PER_WG_ITER (4 * CSA2_MFMA_PROBE_CHAINS * 32768)
+int csa2_mfma_probe(int64_t iters, int32_t workgroups, float* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -109,12 +109,14 @@ _lib.csa2_trace_read.restype = c_int
 _lib.csa2_trace_read.argtypes = [POINTER(TraceRecord), c_int32, POINTER(c_int32)]
 _lib.csa2_read_probe.restype = c_int
 _lib.csa2_read_probe.argtypes = [c_void_p, c_int64, c_void_p, c_void_p]
+_lib.csa2_mfma_probe.restype = c_int
+_lib.csa2_mfma_probe.argtypes = [c_int64, c_int32, c_void_p, c_void_p]
 _lib.csa2_kernel_name.restype = ctypes.c_char_p
 _lib.csa2_kernel_name.argtypes = [c_int32]
 
 EXPORTED = ("csa2_compress", "csa2_index_topk", "csa2_sparse_attn", "csa2_layer_group", "csa2_workspace_size",
             "csa2_status_str", "csa2_last_error", "csa2_abi_version", "csa2_trace_enable", "csa2_trace_read",
-            "csa2_kernel_name", "csa2_grouped_out_proj", "csa2_read_probe",
+            "csa2_kernel_name", "csa2_grouped_out_proj", "csa2_read_probe", "csa2_mfma_probe",
             "csa2_layer_group_noalloc", "csa2_layer_plan")
 
 
@@ -230,6 +232,13 @@ def csa2_trace_read(max_records: int = 65536) -> tuple[list[tuple[str, float]], 
     if n < 0:
         raise Csa2Error(n, "trace read failed")
     return [(csa2_kernel_name(buf[i].kernel), float(buf[i].ms)) for i in range(n)], int(dropped.value)
+
+
+MFMA_PROBE_FLOP_PER_WG_ITER = 4 * 8 * 32768  # CSA2_MFMA_PROBE_FLOP_PER_WG_ITER
+
+
+def csa2_mfma_probe(iters: int, workgroups: int, sink, stream=None) -> None:
+    _check(_lib.csa2_mfma_probe(iters, workgroups, ptr(sink), _stream(stream)))
 
 
 def csa2_read_probe(buf, nbytes: int, sink, stream=None) -> None:

@@ -430,4 +430,20 @@ int csa2_read_probe(const void* buf, int64_t bytes, uint32_t* sink, void* stream
   }
 }
 
+int csa2_mfma_probe(int64_t iters, int32_t workgroups, float* sink, void* stream) {
+  g_last_error.clear();
+  try {
+    if (iters < 1 || iters > (int64_t(1) << 24))
+      return fail(CSA2_ERR_INVALID_ARG, "iters=%lld: need 1..2^24", (long long)iters);
+    if (workgroups < 1 || workgroups > 65536)
+      return fail(CSA2_ERR_INVALID_ARG, "workgroups=%d: need 1..65536", workgroups);
+    if (!sink) return fail(CSA2_ERR_INVALID_ARG, "sink is NULL");
+    clear_stale_error();
+    const hipError_t e = csa2::launch_mfma_probe(iters, workgroups, sink, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? CSA2_OK : fail_hip(e, "matrix-core probe launch");
+  } catch (...) {
+    return fail(CSA2_ERR_HIP, "internal exception");
+  }
+}
+
 }  // extern "C"

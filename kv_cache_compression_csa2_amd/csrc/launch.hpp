@@ -112,6 +112,7 @@ int layer_group_run(const csa2_dims* dims, const csa2_kv_cache* cache, int32_t n
 int set_error(int status, const char* msg);
 
 hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream);
+hipError_t launch_mfma_probe(int64_t iters, int32_t workgroups, float* sink, hipStream_t stream);
 
 hipError_t launch_oproj(int32_t act_dtype, int32_t n_tok, int32_t width, int32_t n_groups, int32_t rank,
                         const void* x, const void* w, void* y, hipStream_t stream);

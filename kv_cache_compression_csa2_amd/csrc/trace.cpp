@@ -135,6 +135,7 @@ const char* csa2_kernel_name(int32_t kernel) {
     case CSA2_KERNEL_OPROJ_MFMA16: return "oproj_mfma16_kernel";
     case CSA2_KERNEL_OPROJ_LDS: return "oproj_lds_kernel";
     case CSA2_KERNEL_READ_PROBE: return "read_probe_kernel";
+    case CSA2_KERNEL_MFMA_PROBE: return "mfma_probe_kernel";
     default: return "unknown";
   }
 }

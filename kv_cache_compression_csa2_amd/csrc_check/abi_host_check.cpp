@@ -188,6 +188,9 @@ int main() {
   EXPECT(csa2_grouped_out_proj(CSA2_BF16, 1, 32767, 8, 1024, fake(), fake(), fake(), nullptr) == CSA2_ERR_INVALID_ARG);
   EXPECT(csa2_grouped_out_proj(CSA2_BF16, 0, 32768, 8, 1024, nullptr, nullptr, nullptr, nullptr) == CSA2_OK);
   EXPECT(csa2_read_probe(fake(), 24, static_cast<uint32_t*>(fake()), nullptr) == CSA2_ERR_INVALID_ARG);
+  EXPECT(csa2_mfma_probe(0, 512, static_cast<float*>(fake()), nullptr) == CSA2_ERR_INVALID_ARG);
+  EXPECT(csa2_mfma_probe(16, 65537, static_cast<float*>(fake()), nullptr) == CSA2_ERR_INVALID_ARG);
+  EXPECT(csa2_mfma_probe(16, 512, nullptr, nullptr) == CSA2_ERR_INVALID_ARG);
   EXPECT(csa2_trace_read(nullptr, -1, nullptr) == CSA2_ERR_INVALID_ARG);
   EXPECT(std::strcmp(csa2_kernel_name(CSA2_KERNEL_SELECT), "select_kernel") == 0);
 

@@ -28,7 +28,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert B.csa2_abi_version() == 6
+    assert B.csa2_abi_version() == 7
     assert B.status_str(0) == "CSA2_OK"
     assert B.status_str(-4) == "CSA2_ERR_MODE_ORDER"
     assert B.status_str(-99) == "CSA2_ERR_UNKNOWN"
@@ -213,6 +213,17 @@ def test_read_probe_rejects_bad_arguments():
     assert lib.csa2_read_probe(FAKE + 8, 1 << 20, FAKE, None) == -1
     assert lib.csa2_read_probe(FAKE, 1 << 20, None, None) == -1
     assert B.csa2_kernel_name(16) == "read_probe_kernel"
+
+
+def test_mfma_probe_rejects_bad_arguments():
+    lib = B.library()
+    assert lib.csa2_mfma_probe(0, 512, FAKE, None) == -1
+    assert lib.csa2_mfma_probe((1 << 24) + 1, 512, FAKE, None) == -1
+    assert lib.csa2_mfma_probe(16, 0, FAKE, None) == -1
+    assert lib.csa2_mfma_probe(16, 65537, FAKE, None) == -1
+    assert lib.csa2_mfma_probe(16, 512, None, None) == -1
+    assert B.csa2_kernel_name(17) == "mfma_probe_kernel"
+    assert B.MFMA_PROBE_FLOP_PER_WG_ITER == 4 * 8 * 32 * 32 * 16 * 2
 
 
 def test_noalloc_group_checks_arguments_and_its_scratch_limit_before_any_hip_call():
