@@ -22,6 +22,9 @@
  *    call returns.
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
  *    default stream).  Results are valid after the caller synchronises.
+ *    csa2_layer_group may run some of its launches on streams of the
+ *    library's own, ordered by events after and before work on `stream`
+ *    (see there); to the caller it behaves as if all ran on `stream`.
  *  - Every argument that the host can check is checked before any HIP call;
  *    a failing check returns a negative csa2_status and enqueues nothing.
  *    Values that live on the device (positions, entry counts, indices) are
@@ -258,6 +261,24 @@ typedef struct csa2_compress_args {
  * reuse flows only from earlier to later layers ([ZB] 3.3.1).
  *  q_pos  [batch][n_q] int32, shared by all layers
  *  ws     at least csa2_workspace_size(..., CSA2_EP_LAYER_GROUP, n_q) bytes
+ *
+ * Attention streams.  An attention launch needs only the top-k of one index
+ * step (its layer's, or its Reuse source's), not the index steps after it
+ * nor the other layers' attention.  When the attention runs one workgroup
+ * per query (128 or more queries per sequence, 64 heads) and the group has
+ * more than one layer, the index steps run in order on `stream` and the
+ * attention launches alternate between the library's two streams of this
+ * device (non-blocking, default priority), each after an event recorded on
+ * `stream` behind the index step that feeds it, each in its own slice of ws;
+ * `stream` then waits for those streams before the call returns, so work
+ * enqueued on `stream` afterwards sees every result.  The events and waits
+ * are captured into a HIP graph as its edges.  Every launch stays on
+ * `stream` otherwise, and also when a buffer one layer writes (out, lse,
+ * topk, pool) overlaps one another layer reads or writes, or when the
+ * streams do not exist yet on this device and `stream` is being captured
+ * (they are created, once, by the first call that is not).  Calls from
+ * several host threads are serialised while they enqueue (one lock for the
+ * library's streams and events).
  */
 int csa2_layer_group(const csa2_dims* dims, const csa2_kv_cache* cache, int32_t n_layers,
                      const csa2_layer* layers, const int32_t* q_pos, int32_t n_q,
@@ -305,8 +326,9 @@ int csa2_layer_plan(int32_t n_layers, const int32_t* ratios, int32_t n_kv, const
  * harnesses that forbid allocation.
  *
  * Same arguments (less the workspace), checks, kernels and results as
- * csa2_layer_group.  The scratch the kernels need (indexer scores, block
- * maxima, attention split partials: csa2_workspace_size(...,
+ * csa2_layer_group, with every launch on `stream` (no attention streams).
+ * The scratch the kernels need (indexer scores, block maxima, one slice of
+ * attention split partials: at most csa2_workspace_size(...,
  * CSA2_EP_LAYER_GROUP, n_q) bytes) lives in a device array inside the
  * library of CSA2_NOALLOC_SCRATCH_BYTES (64 MiB), one copy per GPU, held
  * until the process ends.  That covers decode shapes (one query per
@@ -349,7 +371,8 @@ int csa2_grouped_out_proj(int32_t act_dtype, int32_t n_tok, int32_t width, int32
 
 /* Bytes of workspace an entry point needs for n_q queries per sequence, or 0
  * if the arguments are invalid (csa2_last_error() then says why).  Sized
- * from cache->capacity and cache->batch. */
+ * from cache->capacity and cache->batch.  CSA2_EP_LAYER_GROUP: the index
+ * scratch and one attention slice per attention stream (two). */
 size_t csa2_workspace_size(const csa2_dims* dims, const csa2_kv_cache* cache, int32_t entry_point,
                            int32_t n_q);
 

@@ -738,6 +738,10 @@ AttnPlan plan_attn(const csa2_dims& dims, const csa2_kv_cache& cache, int32_t n_
 
 }  // namespace
 
+bool attn_shares_tiles(const csa2_dims& dims, const csa2_kv_cache& cache, int32_t n_q) {
+  return plan_attn(dims, cache, n_q).share;
+}
+
 size_t attn_workspace_bytes(const csa2_dims& dims, const csa2_kv_cache& cache, int32_t n_q) {
   const AttnPlan p = plan_attn(dims, cache, n_q);
   if (!p.mfma || p.n_splits == 1) return 0;

@@ -98,16 +98,27 @@ hipError_t launch_kernel(int32_t kernel_id, K kern, dim3 grid, dim3 block, size_
 }
 
 size_t attn_workspace_bytes(const csa2_dims& dims, const csa2_kv_cache& cache, int32_t n_q);
+// Whether the attention of n_q queries per sequence runs one workgroup per
+// query whose waves share each row tile (many queries), which leaves compute
+// units free for a second attention launch at the same time.
+bool attn_shares_tiles(const csa2_dims& dims, const csa2_kv_cache& cache, int32_t n_q);
 
 // csa2_layer_group's argument checks and launch sequence with the workspace
 // supplied by get_ws(need, &ws), called once after every argument check
 // passed and before the first launch; a nonzero status from it is returned
 // unchanged.  Errors are recorded as for the entry points; the caller clears
 // the last error and catches exceptions.
+// concurrent: the attention launches may run on the library's own streams
+// (see csa2_layer_group); false keeps every launch on `stream`.
 using WorkspaceFn = std::function<int(size_t need, void** ws)>;
 int layer_group_run(const csa2_dims* dims, const csa2_kv_cache* cache, int32_t n_layers, const csa2_layer* layers,
                     const int32_t* q_pos, int32_t n_q, const csa2_compress_args* compress, const WorkspaceFn& get_ws,
-                    void* stream);
+                    void* stream, bool concurrent);
+// Workspace bytes of a layer group: the index scratch, then one attention
+// workspace per attention stream (`slices`: 1 when every launch stays on
+// the caller's stream, kGroupAttnStreams when they may not).
+constexpr int kGroupAttnStreams = 2;
+size_t layer_group_ws_bytes(const csa2_dims* dims, const csa2_kv_cache* cache, int32_t n_q, int slices);
 // Record `msg` as the last error of this thread and return `status`.
 int set_error(int status, const char* msg);
 

@@ -68,7 +68,7 @@ extern "C" int csa2_layer_group_noalloc(const csa2_dims* dims, const csa2_kv_cac
                                    }
                                    return scratch_address(ws);
                                  },
-                                 stream);
+                                 stream, false);
   } catch (...) {
     return csa2::set_error(CSA2_ERR_HIP, "internal exception");
   }

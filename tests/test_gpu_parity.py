@@ -62,11 +62,14 @@ def test_determinism(runner):
         assert torch.equal(t0, L["topk"]) and torch.equal(o0, L["out"])
 
 
-def test_graph_replay(runner):
-    """A step captured in a HIP graph gives the eager step's outputs on every replay."""
+@pytest.mark.parametrize("name", ["group_small", "replay_small"])
+def test_graph_replay(runner, name):
+    """A step captured in a HIP graph gives the eager step's outputs on every
+    replay (group_small: every launch on the caller's stream; replay_small:
+    the attention launches on the library's two attention streams)."""
     import torch
 
-    wl = synth.get("group_small")
+    wl = synth.get(name)
     inp = synth.Inputs(wl)
     step = runner.DeviceStep(wl, inp)
     step.run()
@@ -86,6 +89,32 @@ def test_graph_replay(runner):
         print(f"[graph] replay {rep}", flush=True)
         for (t0, o0, l0), L in zip(eager, step.layers):
             assert torch.equal(t0, L["topk"]) and torch.equal(o0, L["out"]) and torch.equal(l0, L["lse"])
+
+
+def test_attention_streams_match_one_stream(runner):
+    """A group whose attention launches run on the library's attention streams
+    (replay_small: one workgroup per query, 4 layers) gives bit-identical
+    top-k, outputs and LSE to the same group with every launch on one stream
+    (csa2_layer_group_noalloc keeps them there)."""
+    import torch
+
+    from kv_cache_compression_csa2_amd import binding as B
+
+    wl = synth.get("replay_small")
+    inp = synth.Inputs(wl)
+    st = runner.DeviceStep(wl, inp)
+    st.run()
+    torch.cuda.synchronize()
+    ref = [(L["topk"].clone(), L["out"].clone(), L["lse"].clone()) for L in st.layers]
+    for L in st.layers:
+        L["topk"].fill_(-7)
+        L["out"].fill_(float("nan"))
+        L["lse"].fill_(float("nan"))
+    torch.cuda.synchronize()
+    B.csa2_layer_group_noalloc(st.dims, st.cache.struct(), st.layer_structs(), st.q_pos, wl.n_q, st.compress_args())
+    torch.cuda.synchronize()
+    for li, ((t0, o0, l0), L) in enumerate(zip(ref, st.layers)):
+        assert torch.equal(t0, L["topk"]) and torch.equal(o0, L["out"]) and torch.equal(l0, L["lse"]), li
 
 
 def test_kernel_trace(runner):
