@@ -228,10 +228,19 @@ GroupStreams* group_streams(hipStream_t caller) {
   for (auto& st : g.attn) ok = ok && hipStreamCreateWithFlags(&st, hipStreamNonBlocking) == hipSuccess;
   for (auto& e : g.indexed) ok = ok && hipEventCreateWithFlags(&e, hipEventDisableTiming) == hipSuccess;
   for (auto& e : g.done) ok = ok && hipEventCreateWithFlags(&e, hipEventDisableTiming) == hipSuccess;
-  if (!ok) {
-    for (auto& st : g.attn) if (st) (void)hipStreamDestroy(st), st = nullptr;
-    for (auto& e : g.indexed) if (e) (void)hipEventDestroy(e), e = nullptr;
-    for (auto& e : g.done) if (e) (void)hipEventDestroy(e), e = nullptr;
+  if (!ok) {  // release what was created; the call runs on one stream
+    for (auto& st : g.attn) {
+      if (st) (void)hipStreamDestroy(st);
+      st = nullptr;
+    }
+    for (auto& e : g.indexed) {
+      if (e) (void)hipEventDestroy(e);
+      e = nullptr;
+    }
+    for (auto& e : g.done) {
+      if (e) (void)hipEventDestroy(e);
+      e = nullptr;
+    }
     (void)hipGetLastError();
     return nullptr;
   }
