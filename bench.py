@@ -15,8 +15,10 @@ graph per cache copy; --eager launches them directly).  The same steps are
 then run again with the library's kernel trace on, which brackets every
 kernel with HIP events on its launch stream; the roofline is that of the
 dominant kernel, the full-domain indexer scan: algorithmic HBM bytes per
-launch over its mean duration for decode (one query per sequence), MFMA
-flops per launch for prefill (many queries share each sequence's K).
+launch over its mean duration for decode (one query per sequence; the decode
+scan also writes the step's new entries, so their compress bytes count with
+it), MFMA flops per launch for prefill (many queries share each sequence's
+K).
 
 Prints one JSON line: whole-step tokens/s, the per-kernel device times, the
 scan roofline, and the float64 CPU oracle timed on a bounded sample of the
@@ -102,6 +104,7 @@ def algorithmic_bytes(wl) -> dict:
 
 # sources that define the scan kernels; a counter summary holds their digest
 SCAN_SOURCES = ("kv_cache_compression_csa2_amd/csrc/index_scan.hip",
+                "kv_cache_compression_csa2_amd/csrc/compress_entry.hpp",
                 "kv_cache_compression_csa2_amd/csrc/device_common.hpp")
 
 
@@ -391,6 +394,8 @@ def measure(wl, args) -> dict:
     work = scan_work(wl)
     scan_ms = next(v for k, v in launches if k.startswith("scan_"))
     scan_name = next(k for k, v in launches if k.startswith("scan_"))
+    if scan_name.startswith("scan_fused_"):  # the decode scan also writes the step's entries
+        work = {"bytes": work["bytes"] + nbytes["compress"], "flops": work["flops"]}
     ceiling = None
     if wl.n_q == 1:
         ceiling = read_ceiling(work["bytes"], copies=args.copies)

@@ -262,6 +262,16 @@ typedef struct csa2_compress_args {
  *  q_pos  [batch][n_q] int32, shared by all layers
  *  ws     at least csa2_workspace_size(..., CSA2_EP_LAYER_GROUP, n_q) bytes
  *
+ * One-entry decode steps.  When compress writes one entry per sequence
+ * (n_pos = ratio), n_q = 1, d = 512 and the first layer's index step runs on
+ * the matrix cores over every visible entry (32 x 128 indexer, bf16
+ * activations, a bf16 cache or an FP4 cache with scales per 32), the group
+ * launches no compress kernel: the first index step's scan writes the entry
+ * (its extra workgroups run the compressor, with the same arithmetic and the
+ * same stored bytes, and score the new entry) and the selection folds that
+ * score in (kernel trace: CSA2_KERNEL_SCAN_BF16_FUSED / _FP4_FUSED).  The
+ * results are those of csa2_compress followed by the layers, bit for bit.
+ *
  * Attention streams.  An attention launch needs only the top-k of one index
  * step (its layer's, or its Reuse source's), not the index steps after it
  * nor the other layers' attention.  When the attention runs one workgroup
@@ -409,7 +419,9 @@ typedef enum csa2_kernel {
   CSA2_KERNEL_OPROJ_MFMA16 = 14,  /* oproj_mfma16_kernel (bf16 grouped output projection, <= 16 rows) */
   CSA2_KERNEL_OPROJ_LDS = 15,     /* oproj_lds_kernel (bf16 grouped output projection, 128 x 128 tiles) */
   CSA2_KERNEL_READ_PROBE = 16,    /* read_probe_kernel (csa2_read_probe) */
-  CSA2_KERNEL_MFMA_PROBE = 17     /* mfma_probe_kernel (csa2_mfma_probe) */
+  CSA2_KERNEL_MFMA_PROBE = 17,    /* mfma_probe_kernel (csa2_mfma_probe) */
+  CSA2_KERNEL_SCAN_BF16_FUSED = 18, /* scan_fused_bf16_kernel: bf16 decode scan that writes the step's entry */
+  CSA2_KERNEL_SCAN_FP4_FUSED = 19   /* scan_fused_fp4_kernel: FP4 decode scan that writes the step's entry */
 } csa2_kernel;
 
 typedef struct csa2_trace_record {

@@ -107,7 +107,8 @@ int64_t dom_cap_pool(const csa2_dims* d) { return int64_t(round_up(size_t(d->can
 size_t index_ws_bytes(const csa2_dims* d, const csa2_kv_cache* c, int32_t n_q) {
   const int64_t cap = dom_cap_flat(c) > dom_cap_pool(d) ? dom_cap_flat(c) : dom_cap_pool(d);
   const size_t rows = size_t(c->batch) * size_t(n_q);
-  return round_up(rows * cap * 4, kAlign) + round_up(rows * (cap / 8) * 4, kAlign) + round_up(rows * (cap / 64) * 4, kAlign);
+  return round_up(rows * cap * 4, kAlign) + round_up(rows * (cap / 8) * 4, kAlign) + round_up(rows * (cap / 64) * 4, kAlign) +
+         2 * round_up(rows * 4, kAlign);
 }
 
 csa2::ScanScratch carve_index(void* ws, const csa2_dims* d, const csa2_kv_cache* c, int32_t n_q, bool pool_domain) {
@@ -121,6 +122,11 @@ csa2::ScanScratch carve_index(void* ws, const csa2_dims* d, const csa2_kv_cache*
   s.bmax = reinterpret_cast<float*>(p);
   p += round_up(rows * (cap / 8) * 4, kAlign);
   s.sbmax = reinterpret_cast<float*>(p);
+  p += round_up(rows * (cap / 64) * 4, kAlign);
+  // the step entry's score and id when the decode scan writes the entry
+  s.fix_score = reinterpret_cast<float*>(p);
+  p += round_up(rows * 4, kAlign);
+  s.fix_id = reinterpret_cast<int32_t*>(p);
   return s;
 }
 
@@ -169,10 +175,34 @@ int run_compress(const csa2_dims* d, const csa2_kv_cache* c, const void* latent,
   return e == hipSuccess ? CSA2_OK : fail_hip(e, "compress launch");
 }
 
+// The decode scan writes the step's entry itself (csa2::ScanFuse) when the
+// step compresses one entry per sequence and its first index step scans the
+// whole cache for one query per sequence on the matrix cores: one launch and
+// one pass fewer than the compress kernel followed by the scan.
+bool fuse_compress(const csa2_dims* d, const csa2_kv_cache* c, const csa2_compress_args* compress, int32_t n_q,
+                   const csa2_layer& first) {
+  const bool mfma_shape = d->n_idx_heads == 32 && d->d_idx == 128 && d->act_dtype == CSA2_BF16 &&
+                          (c->kv_dtype == CSA2_BF16 || (c->kv_dtype == CSA2_FP4 && c->idx_group == 32));
+  // the compressing workgroup's 256 threads are laid out for d = 512
+  return compress && compress->n_pos == c->ratio && n_q == 1 && mfma_shape && d->d == 512 &&
+         (first.mode == CSA2_FULL || (first.mode == CSA2_REINDEX && first.source < 0));
+}
+
 int run_index(const csa2_dims* d, const csa2_kv_cache* c, const void* idx_q, const float* head_w,
               const int32_t* q_pos, int32_t n_q, const int32_t* pool_in, int32_t* topk_out, int32_t* pool_out,
-              float* topk_scores, void* ws, hipStream_t s) {
-  const csa2::ScanScratch ss = carve_index(ws, d, c, n_q, pool_in != nullptr);
+              float* topk_scores, void* ws, hipStream_t s, const csa2_compress_args* fused = nullptr) {
+  csa2::ScanScratch ss = carve_index(ws, d, c, n_q, pool_in != nullptr);
+  csa2::ScanFuse fz;
+  if (fused) {
+    fz.cp = csa2::make_compress_params(*d, *c, fused->latent, fused->first_pos, fused->n_pos, fused->pair_logits,
+                                       fused->w_ik);
+    fz.fix_score = const_cast<float*>(ss.fix_score);
+    fz.fix_id = const_cast<int32_t*>(ss.fix_id);
+    ss.fuse = &fz;
+  } else {
+    ss.fix_score = nullptr;
+    ss.fix_id = nullptr;
+  }
   clear_stale_error();
   hipError_t e = csa2::launch_scan(*d, *c, idx_q, head_w, q_pos, n_q, pool_in, ss, s);
   if (e != hipSuccess) return fail_hip(e, "index scan launch");
@@ -367,7 +397,8 @@ int layer_group_run(const csa2_dims* dims, const csa2_kv_cache* cache, int32_t n
   const int n_attn = gs ? kGroupAttnStreams : 0;
   bool used[kGroupAttnStreams] = {};
 
-  if (compress &&
+  const bool fused = fuse_compress(dims, cache, compress, n_q, layers[0]);
+  if (compress && !fused &&
       (st = run_compress(dims, cache, compress->latent, compress->first_pos, compress->n_pos, compress->pair_logits,
                          compress->w_ik, s)))
     return st;
@@ -399,7 +430,8 @@ int layer_group_run(const csa2_dims* dims, const csa2_kv_cache* cache, int32_t n
     if (L.mode == CSA2_FULL || L.mode == CSA2_REINDEX) {
       const int32_t* pool_in = L.mode == CSA2_REINDEX && L.source >= 0 ? layers[L.source].pool : nullptr;
       st = run_index(dims, cache, L.idx_q, L.head_w, q_pos, n_q, pool_in, L.topk,
-                     L.mode == CSA2_FULL && L.make_pool ? L.pool : nullptr, nullptr, ws, s);
+                     L.mode == CSA2_FULL && L.make_pool ? L.pool : nullptr, nullptr, ws, s,
+                     i == 0 && fused ? compress : nullptr);
       if (st) return bail(st);
       if (gs) {
         const hipError_t e = hipEventRecord(gs->indexed[i], s);

@@ -64,17 +64,28 @@ __device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
 
 // E4M3 code of the value nearest to amax/6 (ties to the even code),
 // saturating at 448.  Decided by exact comparisons of amax against 6x the
-// candidate values and midpoints, so no division is rounded.
+// candidate values and midpoints, so no rounded quotient decides it.
 __device__ __forceinline__ uint32_t e4m3_scale_code(double amax) {
   if (!(amax > 0.0)) return 0u;
   if (amax >= 6.0 * 448.0) return 0x7Eu;
-  // largest code c in [0, 0x7E] with 6*value(c) <= amax (values increase with the code)
-  uint32_t lo = 0u, hi = 0x7Eu;
-  while (lo < hi) {
-    const uint32_t mid = (lo + hi + 1u) >> 1;
-    if (6.0 * e4m3_to_f64(mid) <= amax) lo = mid; else hi = mid - 1u;
+  // c = the largest code in [0, 0x7E] with 6*value(c) <= amax (values
+  // increase with the code).  First the largest code whose value is at most
+  // the rounded quotient x = amax / 6, read off x's exponent and leading
+  // significand bits (below 2^-6: the subnormal codes m 2^-9); x lies within
+  // half an ulp of amax / 6 and neighbouring E4M3 values differ by more than
+  // 1/16 of the larger, so no more than one value lies between them and one
+  // exact comparison each way corrects the estimate.
+  const double x = amax / 6.0;
+  uint32_t c;
+  if (x < 0.015625) {
+    c = uint32_t(x * 512.0);  // floor, 0..7
+  } else {
+    const uint64_t u = uint64_t(__double_as_longlong(x));
+    const int ex = int((u >> 52) & 0x7FFu) - 1023;  // -6 .. 8
+    c = min((uint32_t(ex + 7) << 3) | (uint32_t(u >> 49) & 7u), 0x7Eu);
   }
-  const uint32_t c = lo;
+  if (c > 0u && 6.0 * e4m3_to_f64(c) > amax) --c;
+  else if (c < 0x7Eu && 6.0 * e4m3_to_f64(c + 1u) <= amax) ++c;
   if (c == 0x7Eu) return c;
   const double m6 = 3.0 * (e4m3_to_f64(c) + e4m3_to_f64(c + 1u));  // 6 * midpoint, exact
   if (amax > m6) return c + 1u;

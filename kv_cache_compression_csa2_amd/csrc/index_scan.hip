@@ -9,8 +9,7 @@
 //
 // Domain slot i maps to entry j = i (all visible entries) or, with a pool,
 // j = 8 * pool[i / 8] + i % 8.  Slots whose entry is not visible hold -inf.
-#include "device_common.hpp"
-#include "launch.hpp"
+#include "compress_entry.hpp"
 
 namespace csa2 {
 namespace {
@@ -173,6 +172,75 @@ __device__ __forceinline__ int max_row_pairs(int k) {
   return max(int(r[0]), int(r[1]));
 }
 
+// FP4 scans: the indexer query as the fp16 A operand, times 2^k so its
+// largest magnitude sits just below 2^15 (k undone on the score by
+// `unscale`).  The operand is the same for the workgroup's four waves: each
+// converts two of the eight operand chunks of every lane, after one shared
+// maximum fixes k, and all read the whole operand back from LDS
+// ([chunk][lane]).  Every thread of the workgroup calls it.
+// (in two steps: the loads, then the rest, so that a caller can issue the
+// loads early)
+__device__ __forceinline__ void fp4_query_load(const uint16_t* qrow, int h, int wave, uint4 (&qraw)[2]) {
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int q = 2 * wave + c;
+    qraw[c] = *reinterpret_cast<const uint4*>(qrow + 64 * (q >> 2) + 32 * h + 8 * (q & 3));
+  }
+}
+__device__ __forceinline__ const uint4* fp4_query_finish(const uint4 (&qraw)[2], int wave, int lane, float& unscale) {
+  __shared__ uint32_t q_amax[4];
+  __shared__ uint4 q_op[8][64];  // [chunk][lane]
+  uint32_t amax = 0;  // largest |q| (bits of a non-negative float)
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const uint32_t w4[4] = {qraw[c].x, qraw[c].y, qraw[c].z, qraw[c].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) amax = max(amax, max((w4[i] << 16) & 0x7FFF0000u, w4[i] & 0x7FFF0000u));
+  }
+  amax = __ockl_wfred_max_u32(amax);
+  if (lane == 0) q_amax[wave] = amax;
+  __syncthreads();
+  amax = max(max(q_amax[0], q_amax[1]), max(q_amax[2], q_amax[3]));
+  const int e = amax ? int(amax >> 23) - 127 : 0;  // floor(log2 max|q|)
+  const int k = min(100, max(-100, 14 - e));
+  const float up = __uint_as_float(uint32_t(127 + k) << 23);
+  unscale = __uint_as_float(uint32_t(127 - k) << 23);
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const uint32_t w4[4] = {qraw[c].x, qraw[c].y, qraw[c].z, qraw[c].w};
+    uint4 v;
+    uint32_t* vv = reinterpret_cast<uint32_t*>(&v);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f16x2_t pr = {_Float16(__uint_as_float(w4[i] << 16) * up), _Float16(__uint_as_float(w4[i] & 0xFFFF0000u) * up)};
+      vv[i] = __builtin_bit_cast(uint32_t, pr);
+    }
+    q_op[2 * wave + c][lane] = v;
+  }
+  __syncthreads();
+  return &q_op[0][0];
+}
+__device__ __forceinline__ const uint4* fp4_query_lds(const uint16_t* qrow, int h, int wave, int lane,
+                                                      float& unscale) {
+  uint4 qraw[2];
+  fp4_query_load(qrow, h, wave, qraw);
+  return fp4_query_finish(qraw, wave, lane, unscale);
+}
+
+// The score of a tile's entry from its products: the lane's 16 heads'
+// w_h * max(0, logit) in two partial sums (half the dependent chain), plus
+// the other half's 16 (both halves hold the same sum), times `unscale`.
+__device__ __forceinline__ float tile_score(const f32x16_t& acc, const float (&wreg)[16], float unscale) {
+  float part = 0.0f, part1 = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) {
+    part = fmaf(wreg[r], relu(acc[r]), part);
+    part1 = fmaf(wreg[r + 1], relu(acc[r + 1]), part1);
+  }
+  part += part1;
+  return add_halves(part) * unscale;
+}
+
 // Tile loads of one batch (kBatch super-blocks = 2 kBatch tiles of 32 entries).
 template <bool FP4, int kBatch>
 struct ScanBatch {
@@ -183,21 +251,26 @@ struct ScanBatch {
   uint32_t ks[FP4 ? 2 * kBatch : 1];
 };
 
-template <bool FP4, bool POOL, int kBatch, int kSbW, int kAhead>
+// bx: this workgroup's block of super-blocks, b: its sequence (query
+// blockIdx.y); j_skip: an entry left out of
+// the scores and maxima (the step's entry of a fused decode scan; read only
+// when SKIP), or -1.
+template <bool FP4, bool POOL, int kBatch, int kSbW, int kAhead, bool SKIP = false>
 __device__ __forceinline__ void scan_mfma_body(
     int ratio, int64_t capacity, const uint16_t* __restrict__ idx_q, const float* __restrict__ head_w,
     const int32_t* __restrict__ q_pos, int n_q, const int32_t* __restrict__ pool_in, int cand_blocks,
     const uint8_t* __restrict__ idx_k, const uint8_t* __restrict__ idx_scale, const int32_t* __restrict__ n_entries,
-    float* __restrict__ scores, float* __restrict__ bmax, float* __restrict__ sbmax, int64_t dom_cap) {
+    float* __restrict__ scores, float* __restrict__ bmax, float* __restrict__ sbmax, int64_t dom_cap, int bx, int b,
+    int j_skip) {
   constexpr int kTiles = 2 * kBatch;
   constexpr int kIters = kSbW / kBatch;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, h = lane >> 5;
-  const int qi = blockIdx.y, b = blockIdx.z;
+  const int qi = blockIdx.y;
   const int64_t row = int64_t(b) * n_q + qi;
   const int nsb = int(dom_cap / 64);
   const int n_vis = int(visible_count(clamp_entries(n_entries, b, capacity), q_pos[row], ratio));
-  const int sb0 = int(blockIdx.x) * (4 * kSbW) + wave;
+  const int sb0 = bx * (4 * kSbW) + wave;
   const int last_tile = int(idx_rows_padded(capacity) / 32) - 1;
   // this lane's bytes inside a tile: row n, and its half's first chunk
   const uint32_t lane_off = uint32_t(n) * 16u + uint32_t(h) * (FP4 ? 512u : 4096u);
@@ -227,7 +300,7 @@ __device__ __forceinline__ void scan_mfma_body(
         const int blk = sb < nsb && B.slot[t] / 8 < cand_blocks ? prow[B.slot[t] / 8] : -1;
         j = blk >= 0 ? blk * 8 + (B.slot[t] & 7) : -1;
       }
-      B.valid[t] = sb < nsb && j >= 0 && j < n_vis;
+      B.valid[t] = sb < nsb && j >= 0 && j < n_vis && (!SKIP || j != j_skip);
       const uint8_t* tile;
       int jj;  // the entry whose scales are read
       if constexpr (POOL) {
@@ -277,46 +350,7 @@ __device__ __forceinline__ void scan_mfma_body(
   const uint4* q_lds = nullptr;
   float unscale = 1.0f;
   if constexpr (FP4) {
-    // The fp16 query (times 2^k) is the same for the workgroup's four waves:
-    // each converts two of the eight operand chunks of every lane, after one
-    // shared maximum fixes k, and all read the whole operand back from LDS.
-    __shared__ uint32_t q_amax[4];
-    __shared__ uint4 q_op[8][64];  // [chunk][lane]
-    uint4 qraw[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int q = 2 * wave + c;
-      qraw[c] = *reinterpret_cast<const uint4*>(qrow + 64 * (q >> 2) + 32 * h + 8 * (q & 3));
-    }
-    uint32_t amax = 0;  // largest |q| (bits of a non-negative float)
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const uint32_t w4[4] = {qraw[c].x, qraw[c].y, qraw[c].z, qraw[c].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) amax = max(amax, max((w4[i] << 16) & 0x7FFF0000u, w4[i] & 0x7FFF0000u));
-    }
-    amax = __ockl_wfred_max_u32(amax);
-    if (lane == 0) q_amax[wave] = amax;
-    __syncthreads();
-    amax = max(max(q_amax[0], q_amax[1]), max(q_amax[2], q_amax[3]));
-    const int e = amax ? int(amax >> 23) - 127 : 0;  // floor(log2 max|q|)
-    const int k = min(100, max(-100, 14 - e));
-    const float up = __uint_as_float(uint32_t(127 + k) << 23);
-    unscale = __uint_as_float(uint32_t(127 - k) << 23);
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const uint32_t w4[4] = {qraw[c].x, qraw[c].y, qraw[c].z, qraw[c].w};
-      uint4 v;
-      uint32_t* vv = reinterpret_cast<uint32_t*>(&v);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f16x2_t pr = {_Float16(__uint_as_float(w4[i] << 16) * up), _Float16(__uint_as_float(w4[i] & 0xFFFF0000u) * up)};
-        vv[i] = __builtin_bit_cast(uint32_t, pr);
-      }
-      q_op[2 * wave + c][lane] = v;
-    }
-    __syncthreads();
-    q_lds = &q_op[0][0];
+    q_lds = fp4_query_lds(qrow, h, wave, lane, unscale);
   } else {
 #pragma unroll
     for (int q = 0; q < 8; ++q) qop[q] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 64 * h + 8 * q));
@@ -367,20 +401,7 @@ __device__ __forceinline__ void scan_mfma_body(
     }
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
-      float part = 0.0f;
-      {
-        // two partial sums: half the dependent chain
-        float part1 = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          part = fmaf(wreg[r], relu(acc[t][r]), part);
-          part1 = fmaf(wreg[r + 1], relu(acc[t][r + 1]), part1);
-        }
-        part += part1;
-      }
-      // the entry's score: the lane's 16 heads plus the other half's 16
-      // (both halves hold the same sum)
-      float sc = add_halves(part) * unscale;
+      float sc = tile_score(acc[t], wreg, unscale);
       if (!B.valid[t]) sc = -INFINITY;
       // block (8 lanes) and tile (32 lanes) maxima, as ordered integers; the
       // butterflies leave each maximum in every lane it covers
@@ -416,11 +437,141 @@ __device__ __forceinline__ void scan_mfma_body(
 // buffer takes the registers of a third); FP4: one pair per batch at 3.
 template <bool POOL>
 __global__ __launch_bounds__(256, 2) void scan_mfma_bf16_kernel(SCAN_ARGS) {
-  scan_mfma_body<false, POOL, 1, kSbPerWave, 1>(SCAN_PASS);
+  scan_mfma_body<false, POOL, 1, kSbPerWave, 1>(SCAN_PASS, int(blockIdx.x), int(blockIdx.z), -1);
 }
 template <bool POOL>
 __global__ __launch_bounds__(256, 3) void scan_mfma_fp4_kernel(SCAN_ARGS) {
-  scan_mfma_body<true, POOL, 1, kSbPerWave, kFp4Ahead>(SCAN_PASS);
+  scan_mfma_body<true, POOL, 1, kSbPerWave, kFp4Ahead>(SCAN_PASS, int(blockIdx.x), int(blockIdx.z), -1);
+}
+
+// The step's entry of sequence b in a fused decode scan (the compressor's
+// entry 0 at first_pos[b]), or -1 when it writes none.
+__device__ __forceinline__ int fused_entry(const CompressParams& P, int b) {
+  const int64_t fp = P.first_pos[b];
+  if (fp < 0 || fp % P.ratio) return -1;
+  const int64_t j = fp / P.ratio;
+  return j < P.capacity ? int(j) : -1;
+}
+
+// The compressing workgroup of a fused decode scan (sequence b, one query): writes the step's entry with the compressor's arithmetic (256
+// threads standing for the compress kernel's 1024: the same bits), then
+// scores it as the scan scores any entry - the same operands, products in
+// the same order and the same fold - and leaves the score and the entry's id
+// for the selection (fix_score / fix_id: -inf / -1 when the entry is not
+// visible to the query).  The other workgroups leave the entry out.
+//
+// It runs beside a scan that keeps memory busy, where each dependent round
+// trip to memory is slow, so its chain holds as few as it can: the query, the
+// head weights, the latent row and W_ik (all of it for bf16 caches; half,
+// within the FP4 scan's register budget) are requested together up front, the
+// entry is scored from the LDS copy of the stored indexer row (no reload),
+// and its waves take issue priority over the scan's on the compute unit.
+template <bool FP4>
+__device__ void scan_fused_entry(const ScanFuse& fz, int ratio, int64_t capacity, const uint16_t* __restrict__ idx_q,
+                                 const float* __restrict__ head_w, const int32_t* __restrict__ q_pos, int n_q,
+                                 const int32_t* __restrict__ n_entries, int b) {
+  extern __shared__ double csh[];
+  __builtin_amdgcn_s_setprio(2);
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, h = lane >> 5;
+  const int64_t row = int64_t(b) * n_q;
+  // the query operand and head weights, as the scan holds them, requested first
+  const uint16_t* qrow = idx_q + (row * 32 + n) * 128;
+  float wreg[16];
+  auto load_wreg = [&]() {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) wreg[r] = head_w[row * 32 + 8 * (r >> 2) + 4 * h + (r & 3)];
+  };
+  if constexpr (!FP4) load_wreg();  // (FP4: after the entry, within the register budget)
+  bf16x8_t qop[FP4 ? 1 : 8];
+  uint4 qraw[2];
+  if constexpr (FP4) {
+    fp4_query_load(qrow, h, wave, qraw);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) qop[q] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 64 * h + 8 * q));
+  }
+  const int64_t n_vis = visible_count(clamp_entries(n_entries, b, capacity), q_pos[row], ratio);
+  uint8_t* mirror = reinterpret_cast<uint8_t*>(csh + compress_lds_doubles(fz.cp.d, fz.cp.d_idx));
+  const int64_t j = compress_entry<true, 256, FP4 ? 1 : 2, FP4 ? 8 : 16>(fz.cp, 0, b, csh, mirror);
+  float unscale = 1.0f;
+  const uint4* q_lds = nullptr;
+  if constexpr (FP4) load_wreg();
+  if constexpr (FP4) q_lds = fp4_query_finish(qraw, wave, lane, unscale);  // its barrier also publishes mirror
+  else __syncthreads();                                                     // mirror is complete
+  const bool live = j >= 0 && j < n_vis;  // uniform
+  if (live && wave == 0) {
+    // every lane takes the entry's row (column j % 32 is the one kept)
+    f32x16_t acc = f32x16_t{};
+    if constexpr (FP4) {
+      uint4 kf[2];
+#pragma unroll
+      for (int g2 = 0; g2 < 2; ++g2) kf[g2] = *reinterpret_cast<const uint4*>(mirror + 16 * (2 * g2 + h));
+      const uint32_t ks = *reinterpret_cast<const uint32_t*>(mirror + 64) >> (8 * h);
+      float sg[2];
+      uint32_t mp[2];
+      sg[0] = __builtin_amdgcn_cvt_f32_fp8(int(ks), 0);
+      sg[1] = __builtin_amdgcn_cvt_f32_fp8(int(ks), 2);
+      mp[0] = significand_pair(sg[0]);
+      mp[1] = significand_pair(sg[1]);
+#pragma unroll
+      for (int g2 = 0; g2 < 2; ++g2) {
+        const uint32_t w4[4] = {kf[g2].x, kf[g2].y, kf[g2].z, kf[g2].w};
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, q_lds[(4 * g2 + sub) * 64 + lane]),
+                                                       fp4x8_to_f16(w4[sub], sg[g2], mp[g2]), acc, 0, 0, 0);
+      }
+    } else {
+      uint4 kb[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) kb[q] = *reinterpret_cast<const uint4*>(mirror + 2 * (64 * h + 8 * q));
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qop[q], as_bf16x8(kb[q]), acc, 0, 0, 0);
+    }
+    const float sc = tile_score(acc, wreg, unscale);
+    if (lane == int(j & 31)) fz.fix_score[row] = sc;
+  }
+  if (tid == 0) {
+    fz.fix_id[row] = live ? int32_t(j) : -1;
+    if (!live) fz.fix_score[row] = -INFINITY;
+  }
+}
+
+// Decode scan that writes the step's entry, on a one-dimensional grid of
+// batch * (nx + 1) workgroups for one query per sequence: workgroup L <
+// batch compresses and scores sequence L's entry (scan_fused_entry), and
+// workgroup batch + i scans block i % nx of sequence i / nx, as
+// scan_mfma_*_kernel's (x, z), leaving the entry out.  The compressing
+// workgroups come first in dispatch order, so that they start with the scan
+// (placed last, they started only as the first scan workgroups finished and
+// ended after them).  kSbW: super-blocks per scan wave.
+template <bool FP4, int kSbW>
+__device__ __forceinline__ void scan_fused_body(SCAN_ARGS, const ScanFuse& fz) {
+  const int nx = int((dom_cap / 64 + 4 * kSbW - 1) / (4 * kSbW));
+  const int batch = int(gridDim.x) / (nx + 1);
+  const int L = int(blockIdx.x);
+  if (L < batch) {
+    scan_fused_entry<FP4>(fz, ratio, capacity, idx_q, head_w, q_pos, n_q, n_entries, L);
+    return;
+  }
+  const int b = (L - batch) / nx;
+  scan_mfma_body<FP4, false, 1, kSbW, FP4 ? kFp4Ahead : 1, true>(SCAN_PASS, L - batch - b * nx, b,
+                                                                 fused_entry(fz.cp, b));
+}
+// bf16: half-size scan blocks.  The compressing workgroups hold slots that
+// the scan's first wave would use (32K x 16 decode: 512 full-size blocks
+// for 512 resident workgroups), which pushes scan blocks into a later wave;
+// a half-size block ends sooner (32K x 16: 29.3 -> 27.9 us; 256K x 4, which
+// needs several waves anyway: 52.4 against 52.9 us).  One kernel choosing
+// the block size at run time compiled slower than either (29.3 us at 32K).
+constexpr int kFusedSbBf16 = 2;
+constexpr int kFusedSbFp4 = kSbPerWave;
+__global__ __launch_bounds__(256, 2) void scan_fused_bf16_kernel(SCAN_ARGS, ScanFuse fz) {
+  scan_fused_body<false, kFusedSbBf16>(SCAN_PASS, fz);
+}
+__global__ __launch_bounds__(256, 3) void scan_fused_fp4_kernel(SCAN_ARGS, ScanFuse fz) {
+  scan_fused_body<true, kFusedSbFp4>(SCAN_PASS, fz);
 }
 
 // ------------------------------------------------------- query-blocked scan --
@@ -691,6 +842,7 @@ __global__ __launch_bounds__(256, 2) void scan_prefill_kernel(
   }
 }
 
+
 }  // namespace
 
 hipError_t launch_scan(const csa2_dims& dims, const csa2_kv_cache& cache, const void* idx_q, const float* head_w,
@@ -714,6 +866,21 @@ hipError_t launch_scan(const csa2_dims& dims, const csa2_kv_cache& cache, const 
     const int64_t nsb = ss.dom_cap / 64;
     if (nsb > (int64_t(1) << 24) || cache.capacity > (int64_t(1) << 24)) return hipErrorInvalidConfiguration;  // 32-bit slots
     const bool fp4 = cache.kv_dtype == CSA2_FP4;
+    if (ss.fuse) {  // one query per sequence, flat domain (checked by the caller)
+      if (pool_in || n_q != 1) return hipErrorInvalidValue;
+      // the entry's workspace, then the LDS copy of its indexer row
+      const size_t lds = sizeof(double) * size_t(compress_lds_doubles(dims.d, dims.d_idx)) + 2 * size_t(dims.d_idx);
+      if (lds > 64 * 1024) return hipErrorInvalidConfiguration;
+      const int sbw = fp4 ? kFusedSbFp4 : kFusedSbBf16;
+      const int64_t nx = (nsb + 4 * sbw - 1) / (4 * sbw);
+      if ((nx + 1) * cache.batch > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+      const dim3 grid(unsigned((nx + 1) * cache.batch), 1, 1);
+      return launch_kernel(fp4 ? CSA2_KERNEL_SCAN_FP4_FUSED : CSA2_KERNEL_SCAN_BF16_FUSED,
+                           fp4 ? scan_fused_fp4_kernel : scan_fused_bf16_kernel, grid, dim3(256), lds, stream,
+                           cache.ratio, cache.capacity, static_cast<const uint16_t*>(idx_q), head_w, q_pos, n_q,
+                           pool_in, dims.cand_blocks, static_cast<const uint8_t*>(cache.idx_k), cache.idx_scale,
+                           cache.n_entries, ss.scores, ss.bmax, ss.sbmax, ss.dom_cap, *ss.fuse);
+    }
     auto kern = fp4 ? (pool_in ? scan_mfma_fp4_kernel<true> : scan_mfma_fp4_kernel<false>)
                     : (pool_in ? scan_mfma_bf16_kernel<true> : scan_mfma_bf16_kernel<false>);
     const dim3 grid(unsigned((nsb + 4 * kSbPerWave - 1) / (4 * kSbPerWave)), n_q, cache.batch);

@@ -46,12 +46,46 @@ inline RopeTable make_rope_table(const csa2_dims& d) {
   return t;
 }
 
+// Everything the compressor reads and writes (kernel argument).
+struct CompressParams {
+  int d, d_rope, d_idx, kv_dtype, main_group, idx_group, ratio;
+  int64_t capacity;
+  RopeTable rope;
+  const void* latent;        // [batch][n_pos][d] act
+  const int32_t* first_pos;  // [batch]
+  int n_pos;
+  const float* pair_logits;  // [ratio][d], NULL for ratio 1
+  const void* w_ik;          // [d][d_idx] act
+  void* main;
+  uint8_t* main_scale;
+  void* idx_k;
+  uint8_t* idx_scale;
+};
+CompressParams make_compress_params(const csa2_dims& dims, const csa2_kv_cache& cache, const void* latent,
+                                    const int32_t* first_pos, int32_t n_pos, const float* pair_logits,
+                                    const void* w_ik);
+
+// A decode scan that also writes the step's cache entry (one entry per
+// sequence, one query per sequence, d = 512, d_idx = 128, bf16
+// activations): one extra workgroup per sequence runs the compressor, scores
+// the entry and leaves the score and the entry's id in fix_score / fix_id
+// ([batch]); the scan's workgroups leave the entry out, and the selection
+// folds the score back in.
+struct ScanFuse {
+  CompressParams cp;
+  float* fix_score;  // [batch*n_q]
+  int32_t* fix_id;   // [batch*n_q], -1: none
+};
+
 // Scratch layout of one index_topk call (all float32, per (batch, query)).
 struct ScanScratch {
   float* scores;  // [batch*n_q][dom_cap]
   float* bmax;    // [batch*n_q][dom_cap/8]
   float* sbmax;   // [batch*n_q][dom_cap/64]
   int64_t dom_cap;  // multiple of 1024: the decode scan's workgroups cover it exactly
+  const ScanFuse* fuse = nullptr;  // set: the scan writes the step's entry (see ScanFuse)
+  const float* fix_score = nullptr;  // the selection's fold-in of that entry's score, or NULL
+  const int32_t* fix_id = nullptr;
 };
 
 hipError_t launch_compress(const csa2_dims& dims, const csa2_kv_cache& cache, const void* latent,

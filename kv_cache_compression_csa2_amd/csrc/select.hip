@@ -285,13 +285,14 @@ __device__ __forceinline__ void note_key(uint32_t k, uint32_t& cnt, uint32_t& km
 }
 
 // keys[p] = key of src[idx(p)] for p in [0, cnt): kKeyForced where idx(p) is
-// `forced`, kKeyNegInf where idx(p) lies outside [0, n); then put_stats.
-// Each thread issues kPer loads (at clamped, always valid addresses) before
-// it uses any, so the latencies of a batch overlap instead of adding up.
-// n >= 1.
+// `forced`, kKeyNegInf where idx(p) lies outside [0, n), and at least
+// fix_key where idx(p) is fix_at (a score the scan left out: see ScanFuse);
+// then put_stats.  Each thread issues kPer loads (at clamped, always valid
+// addresses) before it uses any, so the latencies of a batch overlap instead
+// of adding up.  n >= 1.
 template <int kPer = 8, class IdxFn>
 __device__ __forceinline__ void gather_keys(const SelLds L, int cnt, const float* __restrict__ src, int n, int forced,
-                                            IdxFn idx) {
+                                            int fix_at, uint32_t fix_key, IdxFn idx) {
   uint32_t c = 0, kmn = 0xFFFFFFFFu, kmx = 0u;
   for (int base = 0; base < cnt; base += kPer * kNT) {
     int id[kPer];
@@ -306,7 +307,8 @@ __device__ __forceinline__ void gather_keys(const SelLds L, int cnt, const float
     for (int i = 0; i < kPer; ++i) {
       const int p = base + i * kNT + int(threadIdx.x);
       if (p < cnt) {
-        const uint32_t k = id[i] == forced ? kKeyForced : ((id[i] >= 0 && id[i] < n) ? score_key(v[i]) : kKeyNegInf);
+        uint32_t k = id[i] == forced ? kKeyForced : ((id[i] >= 0 && id[i] < n) ? score_key(v[i]) : kKeyNegInf);
+        if (id[i] == fix_at) k = max(k, fix_key);
         L.keys[p] = k;
         note_key(k, c, kmn, kmx);
       }
@@ -329,7 +331,9 @@ __device__ __forceinline__ void select_body(int topk, int cand_blocks, int ratio
                                                      const float* __restrict__ scores, const float* __restrict__ bmax,
                                                      const float* __restrict__ sbmax, int64_t dom_cap,
                                                      int32_t* __restrict__ topk_out, int32_t* __restrict__ pool_out,
-                                                     float* __restrict__ topk_scores, int split) {
+                                                     float* __restrict__ topk_scores, int split,
+                                                     const float* __restrict__ fix_score,
+                                                     const int32_t* __restrict__ fix_id) {
   extern __shared__ uint32_t lds_raw[];
   lds_u32* lds = (lds_u32*)lds_raw;  // address-space cast into LDS
   constexpr int kGather = KCAND <= 4096 ? 4 : 8;  // loads in flight per thread in a gather
@@ -358,6 +362,13 @@ __device__ __forceinline__ void select_body(int topk, int cand_blocks, int ratio
   const float* sc = scores + row * dom_cap;
   const float* bm = bmax + row * nb;
   const float* sbm = sbmax + row * nsb;
+  // the entry a fused decode scan left out of its scores and maxima (its
+  // compressing workgroup scored it): folded in at each level
+  constexpr int kNoFix = -0x7FFFFFFF;
+  const int fix_j = fix_id ? fix_id[row] : -1;
+  const uint32_t fix_key = fix_j >= 0 ? score_key(fix_score[row]) : kKeyNegInf;
+  const int fix_blk = fix_j >= 0 ? fix_j / 8 : kNoFix, fix_sb = fix_j >= 0 ? fix_j / 64 : kNoFix;
+  const int fix_ent = fix_j >= 0 ? fix_j : kNoFix;
 
   // ---- HSI pool (full domain only) ----
   // nbsel blocks chosen for the top-k stage, their ids in lb[0 .. nbsel)
@@ -367,17 +378,18 @@ __device__ __forceinline__ void select_body(int topk, int cand_blocks, int ratio
     const int64_t n_vis = visible_count(n, q_pos[row], ratio);
     const int fb = n_vis > 0 ? int((n_vis - 1) / 8) : -1;
     const int fsb = fb >= 0 ? fb / 8 : -1;
-    const uint32_t fkey = fb >= 0 ? score_key(bm[fb]) : kKeyNegInf;  // the forced block's own key
+    uint32_t fkey = fb >= 0 ? score_key(bm[fb]) : kKeyNegInf;  // the forced block's own key
+    if (fb >= 0 && fb == fix_blk) fkey = max(fkey, fix_key);
     int na = nsb;
     if (nsb > cand_blocks) {
-      gather_keys<kGather>(L, nsb, sbm, nsb, fsb, [](int p) { return p; });
+      gather_keys<kGather>(L, nsb, sbm, nsb, fsb, fix_sb, fix_key, [](int p) { return p; });
       __syncthreads();
       na = sel(nsb, cand_blocks, L.la);
     } else {
       for (int p = tid; p < nsb; p += kNT) L.la[p] = uint32_t(p);
       __syncthreads();  // la is read across threads below
     }
-    gather_keys<kGather>(L, 8 * na, bm, nb, fb, [&](int p) { return int(L.la[p >> 3]) * 8 + (p & 7); });
+    gather_keys<kGather>(L, 8 * na, bm, nb, fb, fix_blk, fix_key, [&](int p) { return int(L.la[p >> 3]) * 8 + (p & 7); });
     __syncthreads();
     const int npool = sel(8 * na, cand_blocks, L.lb);
     // the pool members' own keys (the forced block's real maximum in place of
@@ -430,14 +442,14 @@ __device__ __forceinline__ void select_body(int topk, int cand_blocks, int ratio
   if (nbsel < 0) {
     int na = nsb;
     if (nsb > topk) {
-      gather_keys<kGather>(L, nsb, sbm, nsb, -1, [](int p) { return p; });
+      gather_keys<kGather>(L, nsb, sbm, nsb, -1, fix_sb, fix_key, [](int p) { return p; });
       __syncthreads();
       na = sel(nsb, topk, L.la);
     } else {
       for (int p = tid; p < nsb; p += kNT) L.la[p] = uint32_t(p);
       __syncthreads();  // la is read across threads below
     }
-    gather_keys<kGather>(L, 8 * na, bm, nb, -1, [&](int p) { return int(L.la[p >> 3]) * 8 + (p & 7); });
+    gather_keys<kGather>(L, 8 * na, bm, nb, -1, fix_blk, fix_key, [&](int p) { return int(L.la[p >> 3]) * 8 + (p & 7); });
     __syncthreads();
     nbsel = sel(8 * na, topk, L.lb);
     // block ids of the chosen blocks (ascending), in place
@@ -446,7 +458,8 @@ __device__ __forceinline__ void select_body(int topk, int cand_blocks, int ratio
   }
 
   // ---- top-k entries inside the chosen blocks ----
-  gather_keys<kGather>(L, 8 * nbsel, sc, int(dom_cap), -1, [&](int p) { return int(L.lb[p >> 3]) * 8 + (p & 7); });
+  gather_keys<kGather>(L, 8 * nbsel, sc, int(dom_cap), -1, fix_ent, fix_key,
+                       [&](int p) { return int(L.lb[p >> 3]) * 8 + (p & 7); });
   __syncthreads();
   const int ne = sel(8 * nbsel, topk, L.la);
   for (int x = tid; x < topk; x += kNT) {
@@ -454,7 +467,7 @@ __device__ __forceinline__ void select_body(int topk, int cand_blocks, int ratio
     float s = -INFINITY;
     if (x < ne) {
       const int64_t slot = min(int64_t(L.lb[L.la[x] >> 3]) * 8 + (L.la[x] & 7), dom_cap - 1);
-      s = sc[slot];
+      s = slot == fix_ent ? fix_score[row] : sc[slot];
       id = pool_in ? int32_t(int64_t(pool_in[row * cand_blocks + min(slot / 8, int64_t(cand_blocks) - 1)]) * 8 + (slot & 7))
                    : int32_t(slot);
     }
@@ -468,9 +481,11 @@ __device__ __forceinline__ void select_body(int topk, int cand_blocks, int ratio
       const int32_t *__restrict__ pool_in, const int32_t *__restrict__ n_entries,                             \
       const float *__restrict__ scores, const float *__restrict__ bmax, const float *__restrict__ sbmax,       \
       int64_t dom_cap, int32_t *__restrict__ topk_out, int32_t *__restrict__ pool_out,                        \
-      float *__restrict__ topk_scores, int split
-#define SELECT_PASS \
-  topk, cand_blocks, ratio, capacity, q_pos, n_q, pool_in, n_entries, scores, bmax, sbmax, dom_cap, topk_out, pool_out, topk_scores, split
+      float *__restrict__ topk_scores, int split, const float *__restrict__ fix_score,                       \
+      const int32_t *__restrict__ fix_id
+#define SELECT_PASS                                                                                              \
+  topk, cand_blocks, ratio, capacity, q_pos, n_q, pool_in, n_entries, scores, bmax, sbmax, dom_cap, topk_out, pool_out, \
+      topk_scores, split, fix_score, fix_id
 
 __global__ __launch_bounds__(kNT) void select_kernel(SELECT_ARGS) { select_body<kMaxCand>(SELECT_PASS); }
 // two workgroups per compute unit: 32 waves, at most 64 registers each
@@ -511,7 +526,8 @@ hipError_t launch_select(const csa2_dims& dims, const csa2_kv_cache& cache, cons
   const hipError_t err = launch_kernel(CSA2_KERNEL_SELECT, kern, dim3(n_q, cache.batch, split ? 2 : 1), dim3(kNT),
                                        select_lds(small ? kSmallCand : kMaxCand), stream, dims.topk,
                      dims.cand_blocks, cache.ratio, cache.capacity, q_pos, n_q, pool_in, cache.n_entries, ss.scores,
-                     ss.bmax, ss.sbmax, ss.dom_cap, topk_out, pool_out, topk_scores, split);
+                     ss.bmax, ss.sbmax, ss.dom_cap, topk_out, pool_out, topk_scores, split, ss.fix_score,
+                     ss.fix_id);
   return err;
 }
 

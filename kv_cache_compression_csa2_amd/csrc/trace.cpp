@@ -136,6 +136,8 @@ const char* csa2_kernel_name(int32_t kernel) {
     case CSA2_KERNEL_OPROJ_LDS: return "oproj_lds_kernel";
     case CSA2_KERNEL_READ_PROBE: return "read_probe_kernel";
     case CSA2_KERNEL_MFMA_PROBE: return "mfma_probe_kernel";
+    case CSA2_KERNEL_SCAN_BF16_FUSED: return "scan_fused_bf16_kernel";
+    case CSA2_KERNEL_SCAN_FP4_FUSED: return "scan_fused_fp4_kernel";
     default: return "unknown";
   }
 }

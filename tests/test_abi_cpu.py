@@ -223,6 +223,8 @@ def test_mfma_probe_rejects_bad_arguments():
     assert lib.csa2_mfma_probe(16, 65537, FAKE, None) == -1
     assert lib.csa2_mfma_probe(16, 512, None, None) == -1
     assert B.csa2_kernel_name(17) == "mfma_probe_kernel"
+    assert B.csa2_kernel_name(18) == "scan_fused_bf16_kernel"
+    assert B.csa2_kernel_name(19) == "scan_fused_fp4_kernel"
     assert B.MFMA_PROBE_FLOP_PER_WG_ITER == 4 * 8 * 32 * 32 * 16 * 2
 
 

@@ -185,3 +185,67 @@ def test_attention_without_window(mods, name):
             o, _, ls = harness.oc.attention(spec.q[b, qi], t, rows, wl.d_rope, harness.driver.rope_cfg(wl))
             harness.check_outputs(got[b, qi], o, wl, f"{name} seq {b} q {qi} (no window)")
             assert np.allclose(got_lse[b, qi], ls, atol=2e-2 if wl.act == "bf16" else 1e-5), f"{name}: lse"
+
+
+# One-query decode steps with one new entry per sequence, where the layer
+# group's first scan writes the entry itself; per sequence: the usual case,
+# the query one position before the entry's (the entry is hidden from it),
+# fewer entries than the cache holds (the entry past them), and a first
+# position past the cache (nothing written).
+EDGE_CASES = {
+    "decode_edges": replace(synth.get("decode_small"), name="decode_edges", batch=4),
+    "fp4_edges": replace(synth.get("fp4_small"), name="fp4_edges", batch=4, prior=6000),
+}
+
+
+def _edge_inputs(st, wl):
+    st.q_pos[1] -= 1
+    st.cache.n_entries[2] = wl.n_prior_entries - 37
+    st.first_pos[3] = wl.capacity * wl.ratio
+
+
+@pytest.mark.parametrize("name", list(EDGE_CASES))
+def test_fused_decode_entry_edges(mods, name):
+    """The layer group's decode scan that also writes the step's entry gives
+    the same top-k, pool, outputs, LSE and cache bytes, bit for bit, as the
+    separate csa2_compress, csa2_index_topk and csa2_sparse_attn calls."""
+    import torch
+
+    B, R = mods
+    wl = EDGE_CASES[name]
+    inp = synth.Inputs(wl)
+    print(f"[entry] {name}: fused decode entry edges, batch {wl.batch}, kv {wl.kv}", flush=True)
+    fused = R.DeviceStep(wl, inp)
+    sep = R.DeviceStep(wl, inp)
+    _edge_inputs(fused, wl)
+    _edge_inputs(sep, wl)
+    torch.cuda.synchronize()
+    B.csa2_trace_enable(64)
+    try:
+        fused.run()
+        torch.cuda.synchronize()
+        recs, _ = B.csa2_trace_read()
+    finally:
+        B.csa2_trace_enable(0)
+    names = [n for n, _ in recs]
+    assert names[0].startswith("scan_fused_") and "compress_kernel" not in names, names
+
+    cs, ws = sep.cache.struct(), sep.workspace()
+    B.csa2_compress(sep.dims, cs, sep.latent_new, sep.first_pos, wl.new, sep.pair_logits, sep.w_ik)
+    L = sep.layers[0]
+    B.csa2_index_topk(sep.dims, cs, L["q_idx"], L["head_w"], sep.q_pos, wl.n_q, None, L["topk"], L["pool"], None, ws)
+    B.csa2_sparse_attn(sep.dims, cs, L["q"], sep.q_pos, wl.n_q, L["topk"], L["swa"], L["swa_first"],
+                       L["swa"].shape[1], L["out"], L["lse"], ws)
+    torch.cuda.synchronize()
+
+    F = fused.layers[0]
+    for key in ("topk", "out", "lse") + (("pool",) if L["pool"] is not None else ()):
+        assert torch.equal(F[key], L[key]), f"{name}: {key} differs between the fused and the separate calls"
+    for attr in ("main", "main_scale", "idx_store", "idx_scale"):
+        a, b = getattr(fused.cache, attr), getattr(sep.cache, attr)
+        assert (a is None) == (b is None) and (a is None or torch.equal(a, b)), f"{name}: cache {attr} differs"
+    # where the new entry is hidden from the query or past the entries, the top-k leaves it out
+    j = wl.n_prior_entries
+    top = F["topk"].cpu().numpy()
+    for b in (1, 2):
+        assert not (top[b] == j).any(), f"{name}: seq {b} keeps entry {j}"

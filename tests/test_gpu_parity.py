@@ -117,13 +117,17 @@ def test_attention_streams_match_one_stream(runner):
         assert torch.equal(t0, L["topk"]) and torch.equal(o0, L["out"]) and torch.equal(l0, L["lse"]), li
 
 
-def test_kernel_trace(runner):
+@pytest.mark.parametrize("name, first", [
+    ("hsi_small", "scan_fused_bf16_kernel"),  # one-entry decode: the scan writes the entry
+    ("tiny_encoder", "compress_kernel"),
+])
+def test_kernel_trace(runner, name, first):
     """The kernel trace records one positive duration per launch, in launch order."""
     import torch
 
     from kv_cache_compression_csa2_amd import binding as B
 
-    wl = synth.get("hsi_small")
+    wl = synth.get(name)
     inp = synth.Inputs(wl)
     step = runner.DeviceStep(wl, inp)
     B.csa2_trace_enable(64)
@@ -138,6 +142,7 @@ def test_kernel_trace(runner):
     names = [n for n, _ in recs]
     half = len(names) // 2
     assert names[:half] == names[half:]
-    assert names[0] == "compress_kernel" and any(n.startswith("scan_") for n in names)
+    assert names[0] == first and any(n.startswith("scan_") for n in names)
+    assert ("compress_kernel" in names) == (first == "compress_kernel")
     assert "select_kernel" in names and any(n.startswith("attn_") for n in names)
     assert all(ms > 0 for _, ms in recs)
