@@ -98,8 +98,18 @@ __device__ __forceinline__ uint32_t waves_before(const SelLds L, int base, int w
 // histogram (by wave) cut the LDS atomic collisions of clustered keys; three
 // passes always suffice for 32-bit keys.  The compaction is one block-wide
 // scan of packed (greater, equal) counts, then a short walk per thread.
+// The count chosen and t, a key at most the m-th largest (kKeyNegInf when
+// every valid key was chosen): the next level's lower bound.
+struct SelResult {
+  int n;
+  uint32_t t;
+};
+
+// `bound`: a key known to be at most the m-th largest (kKeyNegInf: none).
+// The histogram passes start from the interval [max(bound, min), max]
+// instead of [min, max]; keys below it are never chosen.
 template <bool FINE, int KR>
-__device__ int select_top_impl(const SelLds L, int n, int m, lds_u32* out) {
+__device__ SelResult select_top_impl(const SelLds L, int n, int m, lds_u32* out, uint32_t bound) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int R = ((((n + kNT - 1) / kNT) + 3) & ~3);
   const int p0 = R * tid;
@@ -117,7 +127,7 @@ __device__ int select_top_impl(const SelLds L, int n, int m, lds_u32* out) {
   lds_u32* const hist = FINE ? L.hist : L.hist + kBins * (w & 3);
 
   const uint32_t total = reduce_waves(L, 0, 0);
-  uint32_t lo = reduce_waves(L, kNW, 1), hi = reduce_waves(L, 2 * kNW, 2);
+  uint32_t lo = max(reduce_waves(L, kNW, 1), bound), hi = reduce_waves(L, 2 * kNW, 2);
   // wred is next written by the compaction, or by a pass after its histogram
   // barrier: only the first case needs a barrier here (total is uniform)
   if (total <= uint32_t(m)) __syncthreads();
@@ -231,7 +241,7 @@ __device__ int select_top_impl(const SelLds L, int n, int m, lds_u32* out) {
     eq_run += e;
   }
   __syncthreads();
-  return int(chosen);
+  return SelResult{int(chosen), T};
 }
 
 // 2049..4096 keys with at most a quarter selected: one histogram of
@@ -242,18 +252,18 @@ __device__ int select_top_impl(const SelLds L, int n, int m, lds_u32* out) {
 // pool maxima, still needs a second pass).
 // The register count follows the level's size (4, 8 or 16 keys per thread):
 // a loop over 16 registers holding 4 keys would do 4x the work per pass.
-__device__ __attribute__((noinline)) int select_top(const SelLds L, int n, int m, lds_u32* out) {
-  if (n > 2048 && n <= 4096 && 4 * m <= n) return select_top_impl<true, 4>(L, n, m, out);
-  if (n <= 4 * kNT) return select_top_impl<false, 4>(L, n, m, out);
-  if (n <= 8 * kNT) return select_top_impl<false, 8>(L, n, m, out);
-  return select_top_impl<false, kMaxCand / kNT>(L, n, m, out);
+__device__ __attribute__((noinline)) SelResult select_top(const SelLds L, int n, int m, lds_u32* out, uint32_t bound) {
+  if (n > 2048 && n <= 4096 && 4 * m <= n) return select_top_impl<true, 4>(L, n, m, out, bound);
+  if (n <= 4 * kNT) return select_top_impl<false, 4>(L, n, m, out, bound);
+  if (n <= 8 * kNT) return select_top_impl<false, 8>(L, n, m, out, bound);
+  return select_top_impl<false, kMaxCand / kNT>(L, n, m, out, bound);
 }
 // The same, inlined: the 64-register variant of the kernel must not call a
 // function that allocates beyond that (the full variant keeps the call, whose
 // code measured ~2 us faster per pool selection)
-__device__ __forceinline__ int select_top_inl(const SelLds L, int n, int m, lds_u32* out) {
-  if (n > 2048 && n <= 4096 && 4 * m <= n) return select_top_impl<true, kSmallCand / kNT>(L, n, m, out);
-  return select_top_impl<false, kSmallCand / kNT>(L, n, m, out);
+__device__ __forceinline__ SelResult select_top_inl(const SelLds L, int n, int m, lds_u32* out, uint32_t bound) {
+  if (n > 2048 && n <= 4096 && 4 * m <= n) return select_top_impl<true, kSmallCand / kNT>(L, n, m, out, bound);
+  return select_top_impl<false, kSmallCand / kNT>(L, n, m, out, bound);
 }
 
 // Key of a[i]; an index outside [0, n) (never produced by a correct
@@ -287,30 +297,42 @@ __device__ __forceinline__ void note_key(uint32_t k, uint32_t& cnt, uint32_t& km
 // keys[p] = key of src[idx(p)] for p in [0, cnt): kKeyForced where idx(p) is
 // `forced`, kKeyNegInf where idx(p) lies outside [0, n), and at least
 // fix_key where idx(p) is fix_at (a score the scan left out: see ScanFuse);
-// then put_stats.  Each thread issues kPer loads (at clamped, always valid
-// addresses) before it uses any, so the latencies of a batch overlap instead
-// of adding up.  n >= 1.
-template <int kPer = 8, class IdxFn>
+// then put_stats.  Every level gathers aligned runs: idx(p) = p, or
+// idx(p) = 8 g(p / 8) + p % 8, and cnt and n are multiples of 4 - so four
+// consecutive keys come from four consecutive, 16-byte aligned values, read
+// with one 16-byte load.  Each thread issues kPer such loads (at clamped,
+// always valid addresses) before it uses any, so a level's loads are in
+// flight together (4-byte loads took two dependent batches: 2.6 us for the
+// 4096 block maxima of a 32K decode row).  n >= 4.
+template <int kPer = 4, class IdxFn>
 __device__ __forceinline__ void gather_keys(const SelLds L, int cnt, const float* __restrict__ src, int n, int forced,
                                             int fix_at, uint32_t fix_key, IdxFn idx) {
   uint32_t c = 0, kmn = 0xFFFFFFFFu, kmx = 0u;
-  for (int base = 0; base < cnt; base += kPer * kNT) {
-    int id[kPer];
-    float v[kPer];
+  const int quads = cnt >> 2;
+  for (int base = 0; base < quads; base += kPer * kNT) {
+    int id0[kPer];
+    float4 v[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int p = base + i * kNT + int(threadIdx.x);
-      id[i] = p < cnt ? idx(p) : -1;
-      v[i] = src[min(max(id[i], 0), n - 1)];
+      const int q = base + i * kNT + int(threadIdx.x);
+      id0[i] = q < quads ? idx(4 * q) : -1;
+      v[i] = *reinterpret_cast<const float4*>(src + min(max(id0[i], 0), n - 4));
     }
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int p = base + i * kNT + int(threadIdx.x);
-      if (p < cnt) {
-        uint32_t k = id[i] == forced ? kKeyForced : ((id[i] >= 0 && id[i] < n) ? score_key(v[i]) : kKeyNegInf);
-        if (id[i] == fix_at) k = max(k, fix_key);
-        L.keys[p] = k;
-        note_key(k, c, kmn, kmx);
+      const int q = base + i * kNT + int(threadIdx.x);
+      if (q < quads) {
+        const float vv[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+        uint32_t k4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int id = id0[i] + e;
+          uint32_t k = id == forced ? kKeyForced : ((id >= 0 && id < n) ? score_key(vv[e]) : kKeyNegInf);
+          if (id == fix_at) k = max(k, fix_key);
+          k4[e] = k;
+          note_key(k, c, kmn, kmx);
+        }
+        *reinterpret_cast<lds_u32x4*>(L.keys + 4 * q) = u32x4{k4[0], k4[1], k4[2], k4[3]};
       }
     }
   }
@@ -336,7 +358,7 @@ __device__ __forceinline__ void select_body(int topk, int cand_blocks, int ratio
                                                      const int32_t* __restrict__ fix_id) {
   extern __shared__ uint32_t lds_raw[];
   lds_u32* lds = (lds_u32*)lds_raw;  // address-space cast into LDS
-  constexpr int kGather = KCAND <= 4096 ? 4 : 8;  // loads in flight per thread in a gather
+  constexpr int kGather = KCAND <= 4096 ? 1 : 4;  // 16-byte loads in flight per thread in a gather
   SelLds L;
   L.keys = lds;
   L.la = L.keys + KCAND;
@@ -344,9 +366,20 @@ __device__ __forceinline__ void select_body(int topk, int cand_blocks, int ratio
   L.hist = L.lb + kMaxList;
   L.wred = L.hist + 4 * kBins;
   L.misc = L.wred + 4 * kNW;
+  // Each level's threshold bounds the next level's from below: each of the
+  // m super-blocks (blocks) chosen holds a block (entry) whose key is its
+  // own, at least the threshold, so the next level's m-th largest key is at
+  // least that threshold too (the pool's forced block is forced at both
+  // levels; the pool's top-k over its members' own keys has m <= kappa - 1
+  // members that are not the forced one, each at least the pool threshold).
+  // `bnd` carries it from one selection to the next.
+  uint32_t bnd = kKeyNegInf;
   auto sel = [&](int n, int m, lds_u32* out) {
-    if constexpr (KCAND <= 4096) return select_top_inl(L, n, m, out);
-    else return select_top(L, n, m, out);
+    SelResult r;
+    if constexpr (KCAND <= 4096) r = select_top_inl(L, n, m, out, bnd);
+    else r = select_top(L, n, m, out, bnd);
+    bnd = r.t;
+    return r.n;
   };
   for (int x = threadIdx.x; x < 4 * kBins; x += kNT) L.hist[x] = 0;
 
@@ -440,6 +473,7 @@ __device__ __forceinline__ void select_body(int topk, int cand_blocks, int ratio
 
   // ---- top-k blocks over the whole domain (unless the pool gave them) ----
   if (nbsel < 0) {
+    bnd = kKeyNegInf;  // (a pool's threshold, for kappa places, does not bound k >= kappa)
     int na = nsb;
     if (nsb > topk) {
       gather_keys<kGather>(L, nsb, sbm, nsb, -1, fix_sb, fix_key, [](int p) { return p; });
