@@ -474,21 +474,24 @@ __device__ __forceinline__ void select_body(int topk, int cand_blocks, int ratio
   // ---- top-k blocks over the whole domain (unless the pool gave them) ----
   if (nbsel < 0) {
     bnd = kKeyNegInf;  // (a pool's threshold, for kappa places, does not bound k >= kappa)
-    int na = nsb;
     if (nsb > topk) {
       gather_keys<kGather>(L, nsb, sbm, nsb, -1, fix_sb, fix_key, [](int p) { return p; });
       __syncthreads();
-      na = sel(nsb, topk, L.la);
+      const int na = sel(nsb, topk, L.la);
+      gather_keys<kGather>(L, 8 * na, bm, nb, -1, fix_blk, fix_key,
+                           [&](int p) { return int(L.la[p >> 3]) * 8 + (p & 7); });
+      __syncthreads();
+      nbsel = sel(8 * na, topk, L.lb);
+      // block ids of the chosen blocks (ascending), in place
+      for (int x = tid; x < nbsel; x += kNT) L.lb[x] = L.la[L.lb[x] >> 3] * 8 + (L.lb[x] & 7);
+      __syncthreads();
     } else {
-      for (int p = tid; p < nsb; p += kNT) L.la[p] = uint32_t(p);
-      __syncthreads();  // la is read across threads below
+      // every super-block is kept: the block maxima are gathered in order and
+      // the chosen positions are the block ids (no list, two barriers fewer)
+      gather_keys<kGather>(L, nb, bm, nb, -1, fix_blk, fix_key, [](int p) { return p; });
+      __syncthreads();
+      nbsel = sel(nb, topk, L.lb);
     }
-    gather_keys<kGather>(L, 8 * na, bm, nb, -1, fix_blk, fix_key, [&](int p) { return int(L.la[p >> 3]) * 8 + (p & 7); });
-    __syncthreads();
-    nbsel = sel(8 * na, topk, L.lb);
-    // block ids of the chosen blocks (ascending), in place
-    for (int x = tid; x < nbsel; x += kNT) L.lb[x] = L.la[L.lb[x] >> 3] * 8 + (L.lb[x] & 7);
-    __syncthreads();
   }
 
   // ---- top-k entries inside the chosen blocks ----
