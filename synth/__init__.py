@@ -234,6 +234,10 @@ SMALL = {
                                n_q=200),
     "chunk_fp8win": replace(WORKLOADS["prefill_128k"], name="chunk_fp8win", prior=4096, new=160, n_q=160,
                             swa="fp8"),
+    # one query over a ratio-2 cache whose step writes one entry (two new
+    # positions merged with the per-channel weights)
+    "decode_r2_small": replace(WORKLOADS["decode_32k"], name="decode_r2_small", batch=3, ratio=2, prior=6000, new=2),
+    "fp4_r2_small": replace(WORKLOADS["fp4_1m"], name="fp4_r2_small", batch=2, ratio=2, prior=10000, new=2),
 }
 
 ALL = {**WORKLOADS, **SMALL}

@@ -190,11 +190,13 @@ def test_attention_without_window(mods, name):
 # One-query decode steps with one new entry per sequence, where the layer
 # group's first scan writes the entry itself; per sequence: the usual case,
 # the query one position before the entry's (the entry is hidden from it),
-# fewer entries than the cache holds (the entry past them), and a first
-# position past the cache (nothing written).
+# fewer entries than the cache holds (the entry past them), a first position
+# past the cache (nothing written), and at ratio 2 a first position that is
+# not a whole entry (nothing written).
 EDGE_CASES = {
     "decode_edges": replace(synth.get("decode_small"), name="decode_edges", batch=4),
     "fp4_edges": replace(synth.get("fp4_small"), name="fp4_edges", batch=4, prior=6000),
+    "r2_edges": replace(synth.get("decode_r2_small"), name="r2_edges", batch=5),
 }
 
 
@@ -202,6 +204,8 @@ def _edge_inputs(st, wl):
     st.q_pos[1] -= 1
     st.cache.n_entries[2] = wl.n_prior_entries - 37
     st.first_pos[3] = wl.capacity * wl.ratio
+    if wl.batch > 4:
+        st.first_pos[4] += 1
 
 
 @pytest.mark.parametrize("name", list(EDGE_CASES))
@@ -249,3 +253,5 @@ def test_fused_decode_entry_edges(mods, name):
     top = F["topk"].cpu().numpy()
     for b in (1, 2):
         assert not (top[b] == j).any(), f"{name}: seq {b} keeps entry {j}"
+    if wl.batch > 4:  # no entry written at an odd position: the cache row stays as the prior build left it
+        assert not fused.cache.main[4, j].any() and not sep.cache.main[4, j].any(), f"{name}: seq 4 wrote entry {j}"

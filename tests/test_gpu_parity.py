@@ -17,7 +17,7 @@ SMALL = ["tiny_encoder", "tiny_bf16", "tiny_fp4", "decode_dense", "decode_small"
          "group_small", "fp4_small", "fp4_pages", "pool_mid", "prefill_small", "prefill_fp4_small", "encoder_block_small",
          "tiny_fp8win", "decode_fp8win", "fp4_pages_fp8win", "prefill_fp8win", "prefill_fp4_fp8win",
          "decoder_prefill_small", "tiny_yarn", "decode_yarn", "prefill_yarn", "pool_wide", "topk_wide",
-         "replay_small", "chunk_small", "chunk_fp4_small", "chunk_fp8win"]
+         "replay_small", "chunk_small", "chunk_fp4_small", "chunk_fp8win", "decode_r2_small", "fp4_r2_small"]
 
 
 @pytest.fixture(scope="module")
