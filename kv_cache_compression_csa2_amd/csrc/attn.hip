@@ -291,40 +291,46 @@ __global__ __launch_bounds__(256, SHARE && !FP4 ? 2 : 1) void attn_mfma_kernel(
   const int64_t sfirst = swa ? swa_first[b] : 0;
   const uint16_t* qrow0 = q + (bq * H + hg * 16) * kD;  // finite stand-in for rows with no source
 
-  // kept-entry ids of this workgroup's rows, and the rotation of this query's
-  // position for each rotary pair, once per workgroup
-  int32_t* ids_lds = reinterpret_cast<int32_t*>(lds + (SHARE ? kShareIds : kLdsIds));
-  const int row_lo = tile_lo * 16;
-  {
-    const int r_end = min(tile_hi * 16, topk);
-    int32_t idv[(kMaxIds + 255) / 256];
-#pragma unroll
-    for (int i = 0; i < (kMaxIds + 255) / 256; ++i) {  // all loads first, then the stores
-      const int r = row_lo + tid + 256 * i;
-      idv[i] = r < r_end ? topk_ids[bq * topk + r] : 0;
-    }
-#pragma unroll
-    for (int i = 0; i < (kMaxIds + 255) / 256; ++i) {
-      const int r = row_lo + tid + 256 * i;
-      if (r < r_end) ids_lds[r - row_lo] = idv[i];
-    }
-  }
-  float* rtab = reinterpret_cast<float*>(lds + (SHARE ? kShareRope : kLdsRope));
-  if (tid < d_rope / 2) {
-    const double phi = double(t) * rope.inv_freq[tid];
-    const double two_pi = 6.283185307179586476925, inv_two_pi = 0.15915494309189533577;
-    const float red = float(phi - two_pi * rint(phi * inv_two_pi));  // angle reduced in float64
-    float sn, cs;
-    sincosf(red, &sn, &cs);
-    rtab[2 * tid] = cs;
-    rtab[2 * tid + 1] = sn;
-  }
+  // The workgroup's loads that do not depend on each other go out together,
+  // at addresses that are always valid, with no branch around them (a load
+  // under a branch made the compiler wait for it where the branch joined,
+  // and this prologue took three round trips to memory: 3.5 us of a 12 us
+  // 32K decode workgroup): the query, the rotary frequencies, the kept-entry
+  // ids of the workgroup's rows.
   // B operand of the logits: head l16's query, chunk k = channels chan0(g, k) .. +8
   bf16x8_t qtmp[16];
   {
     const uint16_t* qrow = qrow0 + l16 * kD;
 #pragma unroll
     for (int k = 0; k < 16; ++k) qtmp[k] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + chan0<FP4>(g, k)));
+  }
+  const double inv_freq = rope.inv_freq[min(tid, kMaxRopePairs - 1)];  // used where tid < d_rope / 2
+  int32_t* ids_lds = reinterpret_cast<int32_t*>(lds + (SHARE ? kShareIds : kLdsIds));
+  const int row_lo = tile_lo * 16;
+  const int r_end = min(tile_hi * 16, topk);
+  int32_t idv[(kMaxIds + 255) / 256];
+#pragma unroll
+  for (int i = 0; i < (kMaxIds + 255) / 256; ++i) {
+    const int r = row_lo + tid + 256 * i;
+    // used only where r < r_end; past it, every lane reads the last id it needs
+    idv[i] = topk_ids[bq * topk + min(r, r_end - 1)];
+  }
+  // kept-entry ids of this workgroup's rows, and the rotation of this query's
+  // position for each rotary pair, once per workgroup
+#pragma unroll
+  for (int i = 0; i < (kMaxIds + 255) / 256; ++i) {
+    const int r = row_lo + tid + 256 * i;
+    if (r < r_end) ids_lds[r - row_lo] = idv[i];
+  }
+  float* rtab = reinterpret_cast<float*>(lds + (SHARE ? kShareRope : kLdsRope));
+  if (tid < d_rope / 2) {
+    const double phi = double(t) * inv_freq;
+    const double two_pi = 6.283185307179586476925, inv_two_pi = 0.15915494309189533577;
+    const float red = float(phi - two_pi * rint(phi * inv_two_pi));  // angle reduced in float64
+    float sn, cs;
+    sincosf(red, &sn, &cs);
+    rtab[2 * tid] = cs;
+    rtab[2 * tid + 1] = sn;
   }
   // Complete every load so far with a wait the compiler sees: its own waits
   // count only the loads it knows of, and inside the loop the row copies it

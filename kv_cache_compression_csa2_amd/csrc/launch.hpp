@@ -18,8 +18,9 @@ namespace csa2 {
 // Inverse RoPE frequencies theta^(-2m/d_rope) for pair m, computed once per
 // launch on the host (libm pow, float64) and passed by value to the kernels,
 // so no kernel evaluates a float64 pow per element.
+constexpr int kMaxRopePairs = 64;  // d_rope <= 128
 struct RopeTable {
-  double inv_freq[64];  // angle per position of each rotary pair
+  double inv_freq[kMaxRopePairs];  // angle per position of each rotary pair
   float logit_scale;    // attention logit scale: 1/sqrt(d), times the YaRN temperature
 };
 
