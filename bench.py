@@ -108,12 +108,25 @@ SCAN_SOURCES = ("kv_cache_compression_csa2_amd/csrc/index_scan.hip",
                 "kv_cache_compression_csa2_amd/csrc/device_common.hpp")
 
 
-def sources_digest(paths) -> str:
+def code_digest(texts) -> str:
+    """Digest of source texts with their // comments and blank lines left out
+    (a comment edit leaves the compiled kernels, and so a counter record, as
+    they were)."""
     h = hashlib.sha256()
-    for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+    for text in texts:
+        for line in text.splitlines():
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
+
+
+def sources_digest(paths) -> str:
+    texts = []
+    for p in paths:
+        with open(os.path.join(ROOT, p)) as f:
+            texts.append(f.read())
+    return code_digest(texts)
 
 
 def recorded_traffic(workload: str, kernel: str):

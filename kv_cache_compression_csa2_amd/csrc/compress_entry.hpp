@@ -12,14 +12,15 @@
 // independent float64 computation except when that value sits within float64
 // noise of a rounding boundary.
 //
-// The work of an entry is laid out over 1024 "virtual threads": virtual
-// thread c owns channel c of the merge, the rotation and the row stores, and
-// virtual thread (part, pair) sums projection outputs 2 pair and 2 pair + 1
-// over its slice of input channels.  A block of NT threads runs that layout
-// with thread t standing for virtual threads t, t + NT, t + 2 NT, ...: every
-// sum is formed in the same order at any NT, so the compress kernel (1024
-// threads) and the decode scan's compressing workgroup (256) store the same
-// bits.
+// The compress kernel runs an entry on 1024 threads: thread c owns channel c
+// of the merge, the rotation and the row stores, and thread (part, pair)
+// sums projection outputs 2 pair and 2 pair + 1 over its part's slice of
+// input channels; the parts' partial sums are then added in part order.  The
+// decode scan's compressing workgroup runs the same entry on 256 threads
+// (d = 512, d_idx = 128): thread t owns channels t and t + 256, and in the
+// projection sums outputs 8 (t % 16) .. 8 (t % 16) + 7 over part t / 16.
+// Each output's sum over a part's channels, and over the parts, is formed in
+// the same order in both, so both store the same bits.
 #pragma once
 
 #include "device_common.hpp"

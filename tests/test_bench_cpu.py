@@ -49,3 +49,15 @@ def test_multi_query_rows_count_once():
     rows = 67584 * 1024 + (4096 + 127) * 1024
     per_query = 4096 * (512 * 4 + 2 * 64 * 512 * 2 + 64 * 4)
     assert one_layer == rows + per_query
+
+
+def test_code_digest_ignores_comments_only():
+    """A counter record stays valid across comment edits of the scan sources and
+    is invalidated by any code edit."""
+    import bench
+
+    a = "int f(int x) {  // doubled\n  return 2 * x;\n}\n"
+    b = "// a new header comment\nint f(int x) {  // twice x\n\n  return 2 * x;\n}\n"
+    c = "int f(int x) {\n  return 3 * x;\n}\n"
+    assert bench.code_digest([a]) == bench.code_digest([b])
+    assert bench.code_digest([a]) != bench.code_digest([c])
