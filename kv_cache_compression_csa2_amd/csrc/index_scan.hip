@@ -9,6 +9,8 @@
 //
 // Domain slot i maps to entry j = i (all visible entries) or, with a pool,
 // j = 8 * pool[i / 8] + i % 8.  Slots whose entry is not visible hold -inf.
+#include <atomic>
+
 #include "compress_entry.hpp"
 
 namespace csa2 {
@@ -435,13 +437,15 @@ __device__ __forceinline__ void scan_mfma_body(
 
 // bf16: one super-block pair per batch, 2 waves per SIMD (the double load
 // buffer takes the registers of a third); FP4: one pair per batch at 3.
-template <bool POOL>
+// SBW: super-blocks per wave (kSbPerWave; 2 or 1 when the scan has too few
+// workgroups to cover the compute units, see launch_scan)
+template <bool POOL, int SBW>
 __global__ __launch_bounds__(256, 2) void scan_mfma_bf16_kernel(SCAN_ARGS) {
-  scan_mfma_body<false, POOL, 1, kSbPerWave, 1>(SCAN_PASS, int(blockIdx.x), int(blockIdx.z), -1);
+  scan_mfma_body<false, POOL, 1, SBW, 1>(SCAN_PASS, int(blockIdx.x), int(blockIdx.z), -1);
 }
-template <bool POOL>
+template <bool POOL, int SBW>
 __global__ __launch_bounds__(256, 3) void scan_mfma_fp4_kernel(SCAN_ARGS) {
-  scan_mfma_body<true, POOL, 1, kSbPerWave, kFp4Ahead>(SCAN_PASS, int(blockIdx.x), int(blockIdx.z), -1);
+  scan_mfma_body<true, POOL, 1, SBW, kFp4Ahead>(SCAN_PASS, int(blockIdx.x), int(blockIdx.z), -1);
 }
 
 // The step's entry of sequence b in a fused decode scan (the compressor's
@@ -843,6 +847,26 @@ __global__ __launch_bounds__(256, 2) void scan_prefill_kernel(
 }
 
 
+// Compute units of the current device (looked up once per device).
+hipError_t compute_units(int* cus) {
+  static std::atomic<int> known[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64 && (*cus = known[dev].load(std::memory_order_relaxed)) > 0) return hipSuccess;
+  e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess && dev >= 0 && dev < 64) known[dev].store(*cus, std::memory_order_relaxed);
+  return e;
+}
+
+template <bool FP4, bool POOL>
+auto scan_kernel_for(int sbw) {
+  if constexpr (FP4) return sbw == 1 ? scan_mfma_fp4_kernel<POOL, 1> : sbw == 2 ? scan_mfma_fp4_kernel<POOL, 2>
+                                                                              : scan_mfma_fp4_kernel<POOL, kSbPerWave>;
+  else return sbw == 1 ? scan_mfma_bf16_kernel<POOL, 1> : sbw == 2 ? scan_mfma_bf16_kernel<POOL, 2>
+                                                                  : scan_mfma_bf16_kernel<POOL, kSbPerWave>;
+}
+
 }  // namespace
 
 hipError_t launch_scan(const csa2_dims& dims, const csa2_kv_cache& cache, const void* idx_q, const float* head_w,
@@ -881,9 +905,21 @@ hipError_t launch_scan(const csa2_dims& dims, const csa2_kv_cache& cache, const 
                            pool_in, dims.cand_blocks, static_cast<const uint8_t*>(cache.idx_k), cache.idx_scale,
                            cache.n_entries, ss.scores, ss.bmax, ss.sbmax, ss.dom_cap, *ss.fuse);
     }
-    auto kern = fp4 ? (pool_in ? scan_mfma_fp4_kernel<true> : scan_mfma_fp4_kernel<false>)
-                    : (pool_in ? scan_mfma_bf16_kernel<true> : scan_mfma_bf16_kernel<false>);
-    const dim3 grid(unsigned((nsb + 4 * kSbPerWave - 1) / (4 * kSbPerWave)), n_q, cache.batch);
+    // Few rows (a decode step's pool-domain Reindex scan: 16384 slots per
+    // query, 16 workgroups each) leave most compute units idle and each
+    // workgroup's chain of loads sets the time: smaller blocks, so that the
+    // workgroups at least cover the compute units (4 x 256K Reindex scans
+    // 11.2 / 8.8 -> 5.9 / 4.5 us with 1 super-block per wave); with many
+    // rows (replay segments, prefill chunks) smaller blocks cost more than
+    // they spread (a 128-query replay segment's scans 53-62 -> 71-80 us).
+    int cus = 0;
+    const hipError_t ce = compute_units(&cus);
+    if (ce != hipSuccess) return ce;
+    const int64_t wgs = (nsb + 4 * kSbPerWave - 1) / (4 * kSbPerWave) * n_q * cache.batch;
+    const int sbw = wgs >= cus ? kSbPerWave : (2 * wgs >= cus ? 2 : 1);
+    auto kern = fp4 ? (pool_in ? scan_kernel_for<true, true>(sbw) : scan_kernel_for<true, false>(sbw))
+                    : (pool_in ? scan_kernel_for<false, true>(sbw) : scan_kernel_for<false, false>(sbw));
+    const dim3 grid(unsigned((nsb + 4 * sbw - 1) / (4 * sbw)), n_q, cache.batch);
     const hipError_t err = launch_kernel(cache.kv_dtype == CSA2_FP4 ? CSA2_KERNEL_SCAN_FP4 : CSA2_KERNEL_SCAN_BF16, kern, grid, dim3(256), 0, stream, cache.ratio, cache.capacity,
                        static_cast<const uint16_t*>(idx_q), head_w, q_pos, n_q, pool_in, dims.cand_blocks,
                        static_cast<const uint8_t*>(cache.idx_k), cache.idx_scale, cache.n_entries, ss.scores, ss.bmax,
