@@ -118,6 +118,12 @@ WORKLOADS = {
     ),
 }
 
+# Larger decode batches of the same shape (throughput as the batch grows;
+# measured, not parity cases: the 32K case at batch 16 covers the kernels)
+WORKLOADS["decode_32k_b64"] = replace(
+    WORKLOADS["decode_32k"], name="decode_32k_b64", batch=64,
+    description="decoder-layer decode, bf16: 64 sequences x 32768 context, ratio 1, Full")
+
 # The encoder macro-block: one Full layer that writes the cache and the
 # top-k, then five Reuse layers that attend with their own queries over the
 # same kept entries (zartbot walkthrough, section 2.3.3), on the chunked
