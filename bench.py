@@ -23,8 +23,9 @@ K).
 Prints one JSON line: whole-step tokens/s, the per-kernel device times, the
 scan roofline, and the float64 CPU oracle timed on a bounded sample of the
 same workload on the host cores (all BLAS threads, then one).  Each extra
-workload (--extra, default fp4_1m: 2 x 1M context with FP4 KV) is timed the
-same way in the same run and reported as an object of that line.  Decode
+workload (--extra, default fp4_1m: 2 x 1M context with FP4 KV, and
+group_256k: 4 x 256K through a Full, two Reindex and a Reuse layer) is timed
+the same way in the same run and reported as an object of that line.  Decode
 rooflines carry two denominators: the published 8 TB/s HBM peak and the
 rate the library's streaming-read probe measures for a working set of the
 scan's size on this GPU.
@@ -459,7 +460,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-single-seconds", type=float, default=6.0,
                     help="also time the oracle with BLAS limited to one thread (0 skips it)")
-    ap.add_argument("--extra", default="fp4_1m",
+    ap.add_argument("--extra", default="fp4_1m,group_256k",
                     help="comma-separated workloads timed after the main one and reported as objects of the "
                          "same line ('none' for none)")
     ap.add_argument("--oproj-tokens", type=int, default=0,
