@@ -737,7 +737,11 @@ AttnPlan plan_attn(const csa2_dims& dims, const csa2_kv_cache& cache, int32_t n_
     p.n_blocks = 8 * ((n_bq * p.n_splits + 7) / 8);
     return p;
   }
-  set_splits(n_bq * G, 256);
+  // about 256 workgroups; with fewer than 64 (query, head group) units,
+  // about 128: the splits' partials and their merge then cost more than the
+  // extra parallelism gains (4 x 256K group: 184 -> 180 us; 32K x 16 keeps
+  // 256: 128 took 17.2 against 14.6 us)
+  set_splits(n_bq * G, n_bq * G >= 64 ? 256 : 128);
   p.n_blocks = 8 * G * ((n_bq * p.n_splits + 7) / 8);
   return p;
 }

@@ -4,6 +4,8 @@ caller workspace: two calls in a row on one GPU, the second on a smaller
 shape than the first (so its scratch region still holds the first call's
 data), each bit-identical to the workspace entry point on the same inputs.
 """
+from dataclasses import replace
+
 import pytest
 
 import synth
@@ -11,10 +13,10 @@ import synth
 pytestmark = pytest.mark.gpu
 
 
-def _noalloc_matches_group(R, B, name):
+def _noalloc_matches_group(R, B, wl):
     import torch
 
-    wl = synth.get(name)
+    name = wl.name
     inp = synth.Inputs(wl)
     print(f"[noalloc] {name}: batch {wl.batch}, context {wl.context}, layers {[p.mode for p in wl.layers]}", flush=True)
     st = R.DeviceStep(wl, inp)
@@ -48,6 +50,8 @@ def test_noalloc_group_matches_workspace_group_twice_shrinking():
     from kv_cache_compression_csa2_amd import binding as B
     from kv_cache_compression_csa2_amd import runner as R
 
-    first = _noalloc_matches_group(R, B, "group_small")  # Full(pool) + Reindex x2 + Reuse, 2 x 20001
-    second = _noalloc_matches_group(R, B, "hsi_small")  # Full(pool) + Reindex + Reuse, 2 x 9001
+    big = synth.get("group_small")  # Full(pool) + Reindex x2 + Reuse, 2 x 20001
+    first = _noalloc_matches_group(R, B, big)
+    # the same layers over a shorter context: every buffer of the step smaller
+    second = _noalloc_matches_group(R, B, replace(big, name="group_short", prior=9000))
     assert second < first
