@@ -23,8 +23,8 @@ K).
 Prints one JSON line: whole-step tokens/s, the per-kernel device times, the
 scan roofline, and the float64 CPU oracle timed on a bounded sample of the
 same workload on the host cores (all BLAS threads, then one).  Each extra
-workload (--extra, default fp4_1m: 2 x 1M context with FP4 KV, and
-group_256k: 4 x 256K through a Full, two Reindex and a Reuse layer) is timed
+workload (--extra; by default fp4_1m, 2 x 1M context with FP4 KV, and
+group_256k, 4 x 256K through a Full, two Reindex and a Reuse layer) is timed
 the same way in the same run and reported as an object of that line.  Decode
 rooflines carry two denominators: the published 8 TB/s HBM peak and the
 rate the library's streaming-read probe measures for a working set of the
