@@ -61,3 +61,49 @@ def test_code_digest_ignores_comments_only():
     c = "int f(int x) {\n  return 3 * x;\n}\n"
     assert bench.code_digest([a]) == bench.code_digest([b])
     assert bench.code_digest([a]) != bench.code_digest([c])
+
+
+def test_counter_records_match_the_scan_sources_and_the_accounting():
+    """Each committed HBM counter summary under profiles/ was taken on the scan
+    code as it stands (its digest of the scan sources is the current one, so
+    the bench line reports its traffic), and the algorithmic bytes it divides
+    by are the ones bench.py counts for that kernel and workload today.  A
+    change to the scan sources needs its counters taken again."""
+    import glob
+    import json
+    import os
+
+    paths = sorted(glob.glob(os.path.join(bench.ROOT, "profiles", "*_hbm_counters.txt")))
+    assert paths
+    for path in paths:
+        rec = None
+        with open(path) as f:
+            for line in f:
+                if line.startswith("traffic: "):
+                    rec = json.loads(line[len("traffic: "):])
+        assert rec is not None, path
+        kernel, workload = rec["kernel"], rec["workload"]
+        assert os.path.basename(path) == f"{kernel}_{workload}_hbm_counters.txt"
+        assert rec["sources_sha256"] == bench.sources_digest(bench.SCAN_SOURCES), \
+            f"{path}: taken on other scan sources"
+        assert bench.recorded_traffic(workload, kernel) == rec["bytes_per_launch"]
+        # (each of the three is rounded to a byte on its own)
+        assert abs(rec["bytes_per_launch"] - rec["fetch_bytes_per_launch"] - rec["write_bytes_per_launch"]) <= 1
+        wl = synth.get(workload)
+        alg = bench.scan_work(wl)["bytes"]
+        if kernel.startswith("scan_fused_"):
+            alg += bench.algorithmic_bytes(wl)["compress"]
+        assert rec["algorithmic_bytes_per_launch"] == alg, path
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The library has no multi-GPU path: bench.py says so and exits with 2
+    before it touches a GPU."""
+    import subprocess
+    import sys
+
+    r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=bench.ROOT, capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
