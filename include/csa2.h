@@ -38,6 +38,7 @@
  *
  * Layouts are row-major, innermost index last.  "act" is the activation
  * element type of csa2_dims.act_dtype (float32 or bfloat16 bit patterns).
+ * n_q, the queries per sequence of a call, is 1..65535.
  */
 #ifndef CSA2_H
 #define CSA2_H
@@ -84,13 +85,13 @@ typedef enum csa2_entry_point {
 
 /* Shape of one CSA2 layer ([ZB] section 1.2 hyper-parameters). */
 typedef struct csa2_dims {
-  int32_t d;           /* latent width = query head width (512); multiple of 32 */
+  int32_t d;           /* latent width = query head width (512); a multiple of 32 in 32..1024 */
   int32_t d_rope;      /* trailing rotary channels of the latent (64); even, <= min(d, 128) */
-  int32_t n_heads;     /* main query heads (64) */
-  int32_t n_idx_heads; /* indexer heads (32) */
-  int32_t d_idx;       /* indexer head width = indexer-K width (128); multiple of 32 */
+  int32_t n_heads;     /* main query heads (64); 1..1024 */
+  int32_t n_idx_heads; /* indexer heads (32); n_idx_heads * d_idx <= 8192 */
+  int32_t d_idx;       /* indexer head width = indexer-K width (128); a multiple of 32 up to 512 */
   int32_t topk;        /* entries kept per query (512); 1..2048 */
-  int32_t window;      /* sliding-window rows per query (128); >= 0 */
+  int32_t window;      /* sliding-window rows per query (128); 0..4096 */
   int32_t block_size;  /* HSI block size (8); must be 8 */
   int32_t cand_blocks; /* HSI pool size in blocks (2048); 1..2048 */
   int32_t act_dtype;   /* CSA2_F32 or CSA2_BF16 for latent, W_ik, q, idx_q, window rows, out */
@@ -132,7 +133,7 @@ typedef struct csa2_kv_cache {
   int32_t ratio;      /* compress ratio the entries were made with: 1 or 2 */
   int32_t main_group; /* FP4: channels per scale in main KV: 16 or 32 ([ZB] 2.4.4 says 16) */
   int32_t idx_group;  /* FP4: channels per scale in indexer K: 16 or 32 */
-  int32_t batch;      /* sequences */
+  int32_t batch;      /* sequences; 1..65535 */
   int32_t reserved0;  /* must be 0 */
   int64_t capacity;   /* entry slots per sequence; 1 .. 1048576 */
   void* main;

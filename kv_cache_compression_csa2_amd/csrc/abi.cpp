@@ -490,8 +490,8 @@ size_t csa2_workspace_size(const csa2_dims* dims, const csa2_kv_cache* cache, in
   g_last_error.clear();
   try {
     if (check_dims(dims) || check_cache(dims, cache, false)) return 0;
-    if (n_q <= 0) {
-      fail(CSA2_ERR_INVALID_ARG, "n_q=%d must be positive", n_q);
+    if (n_q <= 0 || n_q > 65535) {  // the calls' range
+      fail(CSA2_ERR_INVALID_ARG, "n_q=%d out of range", n_q);
       return 0;
     }
     switch (entry_point) {

@@ -166,6 +166,10 @@ def test_workspace_size():
     assert B.csa2_workspace_size(d, c, B.EP_LAYER_GROUP, 1) >= n
     with pytest.raises(B.Csa2Error):
         B.csa2_workspace_size(dims(d=3), c, B.EP_INDEX_TOPK, 1)
+    for n_q in (0, 65536):  # outside the calls' 1..65535
+        with pytest.raises(B.Csa2Error):
+            B.csa2_workspace_size(d, c, B.EP_INDEX_TOPK, n_q)
+    assert B.csa2_workspace_size(d, c, B.EP_INDEX_TOPK, 65535) > 0
 
 
 def test_trace_api_without_launches():
