@@ -55,3 +55,41 @@ def test_noalloc_group_matches_workspace_group_twice_shrinking():
     # the same layers over a shorter context: every buffer of the step smaller
     second = _noalloc_matches_group(R, B, replace(big, name="group_short", prior=9000))
     assert second < first
+
+
+def test_noalloc_group_replays_in_a_hip_graph():
+    """The allocation-free entry point captured in a HIP graph, the use it is
+    for: every replay, with eager work and synchronisation between replays,
+    gives the eager call's top-k, pool, outputs and LSE bit for bit (its
+    launches record no memset and stay on the capturing stream)."""
+    import torch
+
+    from kv_cache_compression_csa2_amd import binding as B
+    from kv_cache_compression_csa2_amd import runner as R
+
+    wl = synth.get("group_small")
+    inp = synth.Inputs(wl)
+    st = R.DeviceStep(wl, inp)
+    cache, layers, compress = st.cache.struct(), st.layer_structs(), st.compress_args()
+    # eager first: also this device's first call, which looks up the scratch address
+    B.csa2_layer_group_noalloc(st.dims, cache, layers, st.q_pos, wl.n_q, compress)
+    torch.cuda.synchronize()
+    ref = [{k: (None if L[k] is None else L[k].clone()) for k in ("topk", "pool", "out", "lse")} for L in st.layers]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        B.csa2_layer_group_noalloc(st.dims, cache, layers, st.q_pos, wl.n_q, compress)
+    for rep in range(3):
+        for L in st.layers:  # eager work between replays
+            L["topk"].fill_(-7)
+            L["out"].zero_()
+            L["lse"].zero_()
+            if L["pool"] is not None:
+                L["pool"].fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        print(f"[noalloc] graph replay {rep}", flush=True)
+        for li, (want, L) in enumerate(zip(ref, st.layers)):
+            for k in ("topk", "pool", "out", "lse"):
+                if want[k] is not None:
+                    assert torch.equal(want[k], L[k]), f"replay {rep} layer {li}: {k} differs from the eager call"
