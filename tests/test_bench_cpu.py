@@ -107,3 +107,15 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_cpu_baseline_object():
+    """The cpu_baseline object of the bench line: the oracle's own step on a
+    bounded sample, with the fields the line carries."""
+    wl = synth.get("decode_dense")  # 2 x 401 entries: a step takes milliseconds
+    out = bench.cpu_baseline(wl, 0.3, 0.2)
+    assert out["kind"] == "oracle" and out["unit"] == "tokens/s"
+    assert out["value"] > 0 and out["single_thread_value"] > 0
+    assert isinstance(out["cores"], int) and out["cores"] >= 1
+    assert out["affinity_cores"] >= 1 and out["cpu_model"]
+    assert out["sample"].startswith("decode_dense: sequences [0, 1] of 2")
