@@ -396,6 +396,16 @@ int layer_group_run(const csa2_dims* dims, const csa2_kv_cache* cache, int32_t n
   }
   const int n_attn = gs ? kGroupAttnStreams : 0;
   bool used[kGroupAttnStreams] = {};
+  // On the caller's stream with the workspace's two attention slices, the
+  // row-split attention of consecutive layers alternates between the slices
+  // and one merge launch combines two layers (a kernel boundary and a merge
+  // launch fewer per pair; the same arithmetic, so the same bits): no layer
+  // reads another layer's attention output, and the layers' buffers must not
+  // overlap, since the two merges run in one launch.
+  const bool pair_merges = !gs && concurrent && n_layers > 1 && layers_independent(dims, cache, n_layers, layers, n_q);
+  AttnMerge pending;
+  bool has_pending = false;
+  int slice = 0;
 
   const bool fused = fuse_compress(dims, cache, compress, n_q, layers[0]);
   if (compress && !fused &&
@@ -443,7 +453,7 @@ int layer_group_run(const csa2_dims* dims, const csa2_kv_cache* cache, int32_t n
     // the attention's stream: the caller's, or an attention stream that
     // waits for the index step feeding this layer
     hipStream_t as = s;
-    char* aws = attn_ws;
+    char* aws = pair_merges ? attn_ws + size_t(slice) * attn_bytes : attn_ws;
     if (gs) {
       const int k = next_attn++ % n_attn;
       as = gs->attn[k];
@@ -458,9 +468,27 @@ int layer_group_run(const csa2_dims* dims, const csa2_kv_cache* cache, int32_t n
       if (e != hipSuccess) return bail(fail_hip(e, "reuse top-k copy"));
     }
     clear_stale_error();
-    const hipError_t e = launch_attn(*dims, *cache, L.q, q_pos, n_q, use_topk, L.n_swa ? L.swa_kv : nullptr,
-                                     L.n_swa ? L.swa_first_pos : nullptr, L.n_swa, L.out, L.lse, aws, attn_bytes, as);
+    AttnMerge m;
+    hipError_t e = launch_attn(*dims, *cache, L.q, q_pos, n_q, use_topk, L.n_swa ? L.swa_kv : nullptr,
+                               L.n_swa ? L.swa_first_pos : nullptr, L.n_swa, L.out, L.lse, aws, attn_bytes, as,
+                               pair_merges ? &m : nullptr);
     if (e != hipSuccess) return bail(fail_hip(e, "attention launch"));
+    if (pair_merges && m.n_splits > 0) {
+      if (has_pending) {  // this layer's partials are in the other slice
+        const AttnMerge jobs[2] = {pending, m};
+        e = launch_attn_merge(jobs, 2, s);
+        has_pending = false;
+      } else {
+        pending = m;
+        has_pending = true;
+      }
+      if (e != hipSuccess) return bail(fail_hip(e, "attention merge launch"));
+      slice ^= 1;
+    }
+  }
+  if (has_pending) {
+    const hipError_t e = launch_attn_merge(&pending, 1, s);
+    if (e != hipSuccess) return bail(fail_hip(e, "attention merge launch"));
   }
   if (gs && (st = join())) return st;
   return CSA2_OK;

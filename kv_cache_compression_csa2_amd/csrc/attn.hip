@@ -656,18 +656,28 @@ __global__ __launch_bounds__(256, SHARE && !FP4 ? 2 : 1) void attn_mfma_kernel(
 
 // Combine the split partials of one (query, head): weights exp(m_s - M) / L,
 // computed once by one wave, then each thread adds four channels of every
-// split with 16-byte loads.
+// split with 16-byte loads.  blockIdx.z picks one of up to two merges (two
+// layers of a group whose merges share a launch).
 extern "C" __device__ float __ockl_wfred_max_f32(float);
 extern "C" __device__ float __ockl_wfred_add_f32(float);
 
 constexpr int kMaxSplits = 64;
 
-__global__ __launch_bounds__(128) void attn_merge_kernel(int H, int n_splits, const float* __restrict__ part_o,
-                                                         const float* __restrict__ part_ml,
-                                                         uint16_t* __restrict__ out, float* __restrict__ lse) {
+struct MergeJobs {
+  const float* part_o[2];
+  const float* part_ml[2];
+  uint16_t* out[2];
+  float* lse[2];
+};
+
+__global__ __launch_bounds__(128) void attn_merge_kernel(int H, int n_splits, MergeJobs jobs) {
   __shared__ float wgt[kMaxSplits];
-  const int head = blockIdx.x, tid = threadIdx.x;
+  const int head = blockIdx.x, tid = threadIdx.x, job = blockIdx.z;
   const int64_t bq = blockIdx.y;
+  const float* __restrict__ part_o = jobs.part_o[job];
+  const float* __restrict__ part_ml = jobs.part_ml[job];
+  uint16_t* __restrict__ out = jobs.out[job];
+  float* __restrict__ lse = jobs.lse[job];
   if (tid < kWave) {
     const int64_t at = ((bq * n_splits + tid) * H + head) * 2;
     const float m = tid < n_splits ? part_ml[at] : -INFINITY;
@@ -760,9 +770,29 @@ size_t attn_workspace_bytes(const csa2_dims& dims, const csa2_kv_cache& cache, i
   return o_bytes + rows * 2 * 4;
 }
 
+hipError_t launch_attn_merge(const AttnMerge* jobs, int n_jobs, hipStream_t stream) {
+  if (n_jobs < 1 || n_jobs > 2) return hipErrorInvalidValue;
+  MergeJobs mj{};
+  for (int j = 0; j < n_jobs; ++j) {
+    const AttnMerge& m = jobs[j];
+    if (m.n_splits < 2 || m.n_splits > kMaxSplits || m.n_heads != jobs[0].n_heads ||
+        m.n_splits != jobs[0].n_splits || m.n_bq != jobs[0].n_bq)
+      return hipErrorInvalidValue;
+    mj.part_o[j] = m.part_o;
+    mj.part_ml[j] = m.part_ml;
+    mj.out[j] = m.out;
+    mj.lse[j] = m.lse;
+  }
+  return launch_kernel(CSA2_KERNEL_ATTN_MERGE, attn_merge_kernel,
+                       dim3(unsigned(jobs[0].n_heads), unsigned(jobs[0].n_bq), unsigned(n_jobs)), dim3(128), 0, stream,
+                       jobs[0].n_heads, jobs[0].n_splits, mj);
+}
+
 hipError_t launch_attn(const csa2_dims& dims, const csa2_kv_cache& cache, const void* q, const int32_t* q_pos,
                        int32_t n_q, const int32_t* topk, const void* swa_kv, const int32_t* swa_first_pos,
-                       int32_t n_swa, void* out, float* lse, void* ws, size_t, hipStream_t stream) {
+                       int32_t n_swa, void* out, float* lse, void* ws, size_t, hipStream_t stream,
+                       AttnMerge* merge) {
+  if (merge) *merge = AttnMerge{};
   const AttnPlan p = plan_attn(dims, cache, n_q);
   if (p.mfma) {
     float* part_o = nullptr;
@@ -815,10 +845,19 @@ hipError_t launch_attn(const csa2_dims& dims, const csa2_kv_cache& cache, const 
                                  static_cast<const uint8_t*>(cache.main), cache.main_scale, p.n_tiles,
                                  p.tiles_per_split, p.n_splits, static_cast<uint16_t*>(out), lse, part_o, part_ml);
     if (e != hipSuccess || p.n_splits == 1) return e;
-    const hipError_t err = launch_kernel(CSA2_KERNEL_ATTN_MERGE, attn_merge_kernel,
-                                         dim3(dims.n_heads, unsigned(int64_t(cache.batch) * n_q)), dim3(128), 0,
-                                         stream, dims.n_heads, p.n_splits, part_o, part_ml, static_cast<uint16_t*>(out), lse);
-    return err;
+    AttnMerge m;
+    m.part_o = part_o;
+    m.part_ml = part_ml;
+    m.out = static_cast<uint16_t*>(out);
+    m.lse = lse;
+    m.n_heads = dims.n_heads;
+    m.n_splits = p.n_splits;
+    m.n_bq = int64_t(cache.batch) * n_q;
+    if (merge) {
+      *merge = m;
+      return hipSuccess;
+    }
+    return launch_attn_merge(&m, 1, stream);
   }
   const dim3 grid(dims.n_heads, n_q, cache.batch);
   const size_t lds = sizeof(float) * size_t(dims.d + dims.topk + dims.window + kThreads / 64 + 2);

@@ -101,9 +101,28 @@ hipError_t launch_select(const csa2_dims& dims, const csa2_kv_cache& cache, cons
                          const int32_t* pool_in, const ScanScratch& ss, int32_t* topk_out, int32_t* pool_out,
                          float* topk_scores, hipStream_t stream);
 
+// The merge of a row-split attention launch: its partials (in the launch's
+// workspace) and the outputs the merged rows go to.
+struct AttnMerge {
+  const float* part_o = nullptr;
+  const float* part_ml = nullptr;
+  uint16_t* out = nullptr;
+  float* lse = nullptr;
+  int32_t n_heads = 0;
+  int32_t n_splits = 0;  // 0: the launch was not split, nothing to merge
+  int64_t n_bq = 0;
+};
+
+// With `merge` null a split launch is followed by its merge on `stream`;
+// otherwise the merge is described in *merge and left to the caller
+// (launch_attn_merge), which must run it before the workspace is reused.
 hipError_t launch_attn(const csa2_dims& dims, const csa2_kv_cache& cache, const void* q, const int32_t* q_pos,
                        int32_t n_q, const int32_t* topk, const void* swa_kv, const int32_t* swa_first_pos,
-                       int32_t n_swa, void* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+                       int32_t n_swa, void* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream,
+                       AttnMerge* merge = nullptr);
+// One launch that merges one or two split launches (the same head count,
+// splits and rows): the merges of two layers of a group share a launch.
+hipError_t launch_attn_merge(const AttnMerge* jobs, int n_jobs, hipStream_t stream);
 
 // Kernel trace hooks (trace.cpp).  trace_begin hands out a slot with two
 // events for the next launch (slot -1 and no events when tracing is off);
