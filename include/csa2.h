@@ -290,6 +290,11 @@ typedef struct csa2_compress_args {
  * (they are created, once, by the first call that is not).  Calls from
  * several host threads are serialised while they enqueue (one lock for the
  * library's streams and events).
+ *
+ * Paired merges.  When every launch stays on `stream` and the layers'
+ * buffers are independent (as above), a row-split attention's merge may run
+ * after the next layer's attention, both layers' merges in one launch; each
+ * output element is combined in the same order, so the results are the same.
  */
 int csa2_layer_group(const csa2_dims* dims, const csa2_kv_cache* cache, int32_t n_layers,
                      const csa2_layer* layers, const int32_t* q_pos, int32_t n_q,
